@@ -1,0 +1,12 @@
+"""CPU oracle (test infrastructure only).
+
+Imported by the test suite, by the smoke check and by the benchmark's CPU
+baseline leg, never by the product path.  It shares no code with the HIP
+library.  Parity unpinned: the exact output bits (tolerance only).
+"""
+from .lli8_oracle import *  # noqa: F401,F403
+from .lli8_oracle import (absmax_quantize_rows, decode_bits, dequantize,  # noqa: F401
+                          int8_accumulate, linear_forward, outlier_columns,
+                          quantize_activations, quantize_weight,
+                          quantize_weight_bits, recover_weight,
+                          round_half_away, round_to_dtype_bits)
