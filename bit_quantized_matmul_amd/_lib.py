@@ -1,0 +1,219 @@
+"""ctypes declarations of include/lli8.h and argument marshalling for torch tensors."""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_NAME = "liblli8.so"
+
+LLI8_F16 = 0
+LLI8_BF16 = 1
+
+STATUS = {0: "LLI8_OK", 1: "LLI8_ERR_NULL", 2: "LLI8_ERR_SHAPE", 3: "LLI8_ERR_DTYPE",
+          4: "LLI8_ERR_ALIGN", 5: "LLI8_ERR_THRESHOLD", 6: "LLI8_ERR_UNSUPPORTED",
+          7: "LLI8_ERR_HIP", 8: "LLI8_ERR_WORKSPACE"}
+
+
+class Lli8Error(RuntimeError):
+    def __init__(self, status: int, detail: str):
+        self.status = status
+        self.name = STATUS.get(status, str(status))
+        super().__init__(f"{self.name}: {detail}")
+
+
+class _Workspace(ctypes.Structure):
+    _fields_ = [("CA", ctypes.c_void_p), ("SCA", ctypes.c_void_p), ("bitmap", ctypes.c_void_p),
+                ("idx", ctypes.c_void_p), ("n_idx", ctypes.c_void_p), ("acc", ctypes.c_void_p),
+                ("scratch", ctypes.c_void_p), ("scratch_bytes", ctypes.c_size_t)]
+
+
+TRACE_MAX = 8
+
+
+class _Trace(ctypes.Structure):
+    _fields_ = [("n", ctypes.c_int), ("name", ctypes.c_char_p * TRACE_MAX),
+                ("ms", ctypes.c_float * TRACE_MAX)]
+
+
+def lli8_trace_enable(on: bool = True):
+    lib().lli8_trace_enable(1 if on else 0)
+
+
+def lli8_trace_read():
+    """[(kernel name, ms)] for the kernels enqueued since the previous read (waits for them)."""
+    t = _Trace()
+    _check(lib().lli8_trace_read(ctypes.byref(t)))
+    return [(t.name[i].decode(), float(t.ms[i])) for i in range(t.n)]
+
+
+def library_path() -> str:
+    return os.environ.get("LLI8_LIBRARY", os.path.join(HERE, LIB_NAME))
+
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded library; raises if it has not been built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    path = library_path()
+    if not os.path.exists(path):
+        raise ImportError(f"{path} not found: build it with `python -m bit_quantized_matmul_amd.build`"
+                          " (the HIP library is required; there is no CPU fallback)")
+    L = ctypes.CDLL(path)
+    i64, vp, f32, i32 = ctypes.c_int64, ctypes.c_void_p, ctypes.c_float, ctypes.c_int
+    L.lli8_quant_weight_rowwise.argtypes = [vp, i64, i64, i32, vp, vp, vp]
+    L.lli8_quant_weight_rowwise.restype = i32
+    L.lli8_quant_rowwise_outliers.argtypes = [vp, i64, i64, i32, f32, vp, vp, vp, vp, vp, vp]
+    L.lli8_quant_rowwise_outliers.restype = i32
+    L.lli8_int8_linear.argtypes = [vp, i64, i64, i64, i32, vp, vp, vp, f32, vp,
+                                   ctypes.POINTER(_Workspace), vp]
+    L.lli8_int8_linear.restype = i32
+    L.lli8_scratch_bytes.argtypes = [i64, i64, i32]
+    L.lli8_scratch_bytes.restype = ctypes.c_size_t
+    L.lli8_status_string.argtypes = [i32]
+    L.lli8_status_string.restype = ctypes.c_char_p
+    L.lli8_last_error.argtypes = []
+    L.lli8_last_error.restype = ctypes.c_char_p
+    L.lli8_version.argtypes = []
+    L.lli8_version.restype = ctypes.c_char_p
+    L.lli8_trace_enable.argtypes = [i32]
+    L.lli8_trace_enable.restype = None
+    L.lli8_trace_read.argtypes = [ctypes.POINTER(_Trace)]
+    L.lli8_trace_read.restype = i32
+    _lib = L
+    return L
+
+
+def _check(status: int):
+    if status != 0:
+        raise Lli8Error(status, lib().lli8_last_error().decode())
+
+
+def lli8_version() -> str:
+    return lib().lli8_version().decode()
+
+
+def lli8_status_string(status: int) -> str:
+    return lib().lli8_status_string(status).decode()
+
+
+def lli8_scratch_bytes(T: int, K: int, dtype: int = LLI8_F16) -> int:
+    return int(lib().lli8_scratch_bytes(T, K, dtype))
+
+
+# ------------------------------------------------------------ torch glue ----
+
+def _torch():
+    import torch
+    return torch
+
+
+def _dt(t) -> int:
+    torch = _torch()
+    if t.dtype == torch.float16:
+        return LLI8_F16
+    if t.dtype == torch.bfloat16:
+        return LLI8_BF16
+    raise TypeError(f"dtype {t.dtype} is not float16 or bfloat16")
+
+
+def _ptr(t) -> Optional[int]:
+    if t is None:
+        return None
+    if not t.is_contiguous():
+        raise ValueError("tensors passed to lli8 must be contiguous")
+    return t.data_ptr()
+
+
+def _stream(device, stream=None) -> int:
+    if stream is not None:
+        return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+    return _torch().cuda.current_stream(device).cuda_stream
+
+
+def lli8_quant_weight_rowwise(W, CB=None, SCB=None, stream=None):
+    """W [N, K] fp16/bf16 on the GPU -> (CB int8 [N, K], SCB fp32 [N])."""
+    torch = _torch()
+    N, K = W.shape
+    if CB is None:
+        CB = torch.empty((N, K), dtype=torch.int8, device=W.device)
+    if SCB is None:
+        SCB = torch.empty((N,), dtype=torch.float32, device=W.device)
+    _check(lib().lli8_quant_weight_rowwise(_ptr(W), N, K, _dt(W), _ptr(CB), _ptr(SCB),
+                                           _stream(W.device, stream)))
+    return CB, SCB
+
+
+def lli8_quant_rowwise_outliers(X, threshold: float, CA=None, SCA=None, bitmap=None, idx=None,
+                                n_idx=None, stream=None):
+    """X [T, K] -> (CA, SCA, bitmap, idx, n_idx); idx[:n_idx] are the outlier columns."""
+    torch = _torch()
+    X2 = X.reshape(-1, X.shape[-1])
+    T, K = X2.shape
+    dev = X.device
+    CA = torch.empty((T, K), dtype=torch.int8, device=dev) if CA is None else CA
+    SCA = torch.empty((T,), dtype=torch.float32, device=dev) if SCA is None else SCA
+    bitmap = torch.empty(((K + 31) // 32,), dtype=torch.int32, device=dev) if bitmap is None else bitmap
+    idx = torch.empty((K,), dtype=torch.int32, device=dev) if idx is None else idx
+    n_idx = torch.empty((1,), dtype=torch.int32, device=dev) if n_idx is None else n_idx
+    _check(lib().lli8_quant_rowwise_outliers(_ptr(X2), T, K, _dt(X2), float(threshold), _ptr(CA),
+                                             _ptr(SCA), _ptr(bitmap), _ptr(idx), _ptr(n_idx),
+                                             _stream(dev, stream)))
+    return CA, SCA, bitmap, idx, n_idx
+
+
+class Workspace:
+    """Caller-owned buffers of one forward call (torch tensors on one device)."""
+
+    def __init__(self, T: int, K: int, N: int, dtype, device, want_acc: bool = False):
+        torch = _torch()
+        self.T, self.K, self.N = T, K, N
+        self.CA = torch.empty((T, K), dtype=torch.int8, device=device)
+        self.SCA = torch.empty((max(T, 1),), dtype=torch.float32, device=device)
+        self.bitmap = torch.empty(((K + 31) // 32,), dtype=torch.int32, device=device)
+        self.idx = torch.empty((K,), dtype=torch.int32, device=device)
+        self.n_idx = torch.zeros((1,), dtype=torch.int32, device=device)
+        self.acc = torch.empty((T, N), dtype=torch.int32, device=device) if want_acc else None
+        nbytes = lli8_scratch_bytes(T, K, LLI8_F16)
+        self.scratch = torch.empty((max(nbytes, 16),), dtype=torch.uint8, device=device)
+        self._struct = _Workspace(self.CA.data_ptr(), self.SCA.data_ptr(), self.bitmap.data_ptr(),
+                                  self.idx.data_ptr(), self.n_idx.data_ptr(),
+                                  self.acc.data_ptr() if self.acc is not None else None,
+                                  self.scratch.data_ptr(), nbytes)
+
+    def fits(self, T, K, N, want_acc) -> bool:
+        return (T, K, N) == (self.T, self.K, self.N) and (self.acc is not None or not want_acc)
+
+    def outlier_columns(self):
+        """The ascending outlier columns of the last call (copies to the host)."""
+        n = int(self.n_idx.item())
+        return self.idx[:n].cpu()
+
+
+def lli8_int8_linear(X, CB, SCB, bias=None, threshold: float = 6.0, out=None,
+                     ws: Optional[Workspace] = None, want_acc: bool = False, stream=None):
+    """out = LLM.int8() forward of X [..., K] with the int8 weight (CB, SCB).
+
+    Returns (out, ws); ws holds CA, SCA, bitmap, idx, n_idx (and acc when
+    want_acc) of this call.
+    """
+    torch = _torch()
+    lead = X.shape[:-1]
+    X2 = X.reshape(-1, X.shape[-1])
+    T, K = X2.shape
+    N = CB.shape[0]
+    if CB.shape[1] != K:
+        raise ValueError(f"CB has K={CB.shape[1]}, X has K={K}")
+    if ws is None or not ws.fits(T, K, N, want_acc):
+        ws = Workspace(T, K, N, X.dtype, X.device, want_acc)
+    if out is None:
+        out = torch.empty((T, N), dtype=X.dtype, device=X.device)
+    _check(lib().lli8_int8_linear(_ptr(X2), T, K, N, _dt(X2), _ptr(CB), _ptr(SCB), _ptr(bias),
+                                  float(threshold), _ptr(out), ctypes.byref(ws._struct),
+                                  _stream(X.device, stream)))
+    return out.reshape(*lead, N), ws

@@ -1,0 +1,245 @@
+// C-ABI of the lli8 library: argument validation, then kernel launches on the
+// caller's stream.  Every argument is checked before anything is enqueued, so
+// a rejected call writes nothing.  No exception crosses the interface.
+#include <math.h>
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include <hip/hip_runtime.h>
+
+#include "../../include/lli8.h"
+#include "lli8_internal.h"
+
+namespace {
+
+constexpr int64_t kMaxK = 133144;  // K * 127^2 < 2^31: int32 accumulators stay exact
+
+thread_local char g_err[512] = "";
+
+lli8_status_t fail(lli8_status_t st, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
+lli8_status_t fail(lli8_status_t st, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof g_err, fmt, ap);
+  va_end(ap);
+  return st;
+}
+
+lli8_status_t hip_status(hipError_t e, const char* where) {
+  if (e == hipSuccess) return LLI8_OK;
+  return fail(LLI8_ERR_HIP, "%s: %s", where, hipGetErrorString(e));
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+lli8_status_t check_dtype(lli8_dtype_t dt) {
+  if (dt != LLI8_F16 && dt != LLI8_BF16) return fail(LLI8_ERR_DTYPE, "dtype %d is not F16 (0) or BF16 (1)", (int)dt);
+  return LLI8_OK;
+}
+
+lli8_status_t check_sizes(int64_t T, int64_t K, int64_t N) {
+  if (T < 0 || K < 1 || N < 1) return fail(LLI8_ERR_SHAPE, "bad sizes T=%lld K=%lld N=%lld", (long long)T, (long long)K, (long long)N);
+  if (K > kMaxK) return fail(LLI8_ERR_UNSUPPORTED, "K=%lld above %lld (int32 accumulator headroom)", (long long)K, (long long)kMaxK);
+  if (T > INT32_MAX || N > INT32_MAX || T * K > ((int64_t)1 << 40) || N * K > ((int64_t)1 << 40))
+    return fail(LLI8_ERR_UNSUPPORTED, "sizes too large T=%lld K=%lld N=%lld", (long long)T, (long long)K, (long long)N);
+  return LLI8_OK;
+}
+
+#define REQUIRE(p, name)                                                       \
+  do {                                                                         \
+    if ((p) == nullptr) return fail(LLI8_ERR_NULL, "%s is NULL", name);       \
+    if (!aligned16(p)) return fail(LLI8_ERR_ALIGN, "%s is not 16-byte aligned", name); \
+  } while (0)
+
+#define OPTIONAL(p, name)                                                      \
+  do {                                                                         \
+    if ((p) != nullptr && !aligned16(p)) return fail(LLI8_ERR_ALIGN, "%s is not 16-byte aligned", name); \
+  } while (0)
+
+#define TRY(x)                                                                 \
+  do {                                                                         \
+    lli8_status_t st_ = (x);                                                   \
+    if (st_ != LLI8_OK) return st_;                                            \
+  } while (0)
+
+// ---- optional kernel timing (lli8_trace_*) ----
+struct Trace {
+  bool on = false;
+  bool created = false;
+  int n = 0;
+  const char* name[LLI8_TRACE_MAX];
+  hipEvent_t ev[2 * LLI8_TRACE_MAX];
+};
+Trace g_trace;
+
+lli8_status_t trace_begin(hipStream_t s, const char* name) {
+  if (!g_trace.on) return LLI8_OK;
+  if (!g_trace.created) {
+    for (int i = 0; i < 2 * LLI8_TRACE_MAX; ++i) {
+      hipError_t e = hipEventCreate(&g_trace.ev[i]);
+      if (e != hipSuccess) return hip_status(e, "trace event create");
+    }
+    g_trace.created = true;
+  }
+  if (g_trace.n >= LLI8_TRACE_MAX) return LLI8_OK;
+  g_trace.name[g_trace.n] = name;
+  return hip_status(hipEventRecord(g_trace.ev[2 * g_trace.n], s), "trace event record");
+}
+
+lli8_status_t trace_end(hipStream_t s) {
+  if (!g_trace.on || g_trace.n >= LLI8_TRACE_MAX) return LLI8_OK;
+  lli8_status_t st = hip_status(hipEventRecord(g_trace.ev[2 * g_trace.n + 1], s), "trace event record");
+  g_trace.n++;
+  return st;
+}
+
+#define TRACED(stream, name, launch)                                           \
+  do {                                                                         \
+    TRY(trace_begin(stream, name));                                            \
+    TRY(hip_status((launch), name));                                           \
+    TRY(trace_end(stream));                                                    \
+  } while (0)
+
+// Outliers are looked for only for a finite positive threshold.
+bool outliers_enabled(float tau) { return tau > 0.0f && isfinite(tau); }
+
+lli8_status_t enqueue_activation_split(const void* X, int64_t T, int64_t K, int dt, float tau, int8_t* CA,
+                                       float* SCA, uint32_t* bitmap, int32_t* idx, int32_t* n_idx, void* xo,
+                                       hipStream_t s) {
+  const int64_t W = (K + 31) / 32;
+  TRACED(s, "bitmap_clear", lli8::launch_fill_u32(bitmap, W, 0u, s));
+  if (outliers_enabled(tau)) TRACED(s, "outlier_scan", lli8::launch_scan_outliers(dt, X, T, K, tau, bitmap, s));
+  TRACED(s, "quant_activations", lli8::launch_quant_act(dt, X, T, K, bitmap, CA, SCA, idx, n_idx, xo, s));
+  return LLI8_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* lli8_version(void) { return "0.1.0"; }
+
+void lli8_trace_enable(int on) { g_trace.on = on != 0; }
+
+lli8_status_t lli8_trace_read(lli8_trace_t* out) {
+  if (out == nullptr) return fail(LLI8_ERR_NULL, "trace output is NULL");
+  out->n = 0;
+  for (int i = 0; i < g_trace.n; ++i) {
+    TRY(hip_status(hipEventSynchronize(g_trace.ev[2 * i + 1]), "trace event wait"));
+    float ms = 0.0f;
+    TRY(hip_status(hipEventElapsedTime(&ms, g_trace.ev[2 * i], g_trace.ev[2 * i + 1]), "trace elapsed"));
+    out->name[i] = g_trace.name[i];
+    out->ms[i] = ms;
+    out->n = i + 1;
+  }
+  g_trace.n = 0;
+  return LLI8_OK;
+}
+
+const char* lli8_last_error(void) { return g_err; }
+
+const char* lli8_status_string(lli8_status_t s) {
+  switch (s) {
+    case LLI8_OK: return "ok";
+    case LLI8_ERR_NULL: return "required pointer is NULL";
+    case LLI8_ERR_SHAPE: return "invalid shape";
+    case LLI8_ERR_DTYPE: return "invalid dtype";
+    case LLI8_ERR_ALIGN: return "pointer not 16-byte aligned";
+    case LLI8_ERR_THRESHOLD: return "threshold is NaN";
+    case LLI8_ERR_UNSUPPORTED: return "unsupported size";
+    case LLI8_ERR_HIP: return "HIP runtime error";
+    case LLI8_ERR_WORKSPACE: return "scratch buffer missing or too small";
+  }
+  return "unknown status";
+}
+
+size_t lli8_scratch_bytes(int64_t T, int64_t K, lli8_dtype_t dtype) {
+  (void)dtype;  // both dtypes are 16-bit
+  if (T <= 0 || K <= 0) return 0;
+  const int64_t kpad = (K + 31) / 32 * 32;
+  return (size_t)(T * kpad * 2);
+}
+
+lli8_status_t lli8_quant_weight_rowwise(const void* W, int64_t N, int64_t K, lli8_dtype_t dtype, int8_t* CB,
+                                        float* SCB, void* stream) {
+  TRY(check_dtype(dtype));
+  if (N < 0 || K < 1) return fail(LLI8_ERR_SHAPE, "bad sizes N=%lld K=%lld", (long long)N, (long long)K);
+  if (K > kMaxK) return fail(LLI8_ERR_UNSUPPORTED, "K=%lld above %lld", (long long)K, (long long)kMaxK);
+  REQUIRE(W, "W");
+  REQUIRE(CB, "CB");
+  REQUIRE(SCB, "SCB");
+  if (N == 0) return LLI8_OK;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  TRACED(s, "quant_weight", lli8::launch_quant_weight((int)dtype, W, N, K, CB, SCB, s));
+  return LLI8_OK;
+}
+
+lli8_status_t lli8_quant_rowwise_outliers(const void* X, int64_t T, int64_t K, lli8_dtype_t dtype, float threshold,
+                                          int8_t* CA, float* SCA, uint32_t* bitmap, int32_t* idx, int32_t* n_idx,
+                                          void* stream) {
+  TRY(check_dtype(dtype));
+  TRY(check_sizes(T, K, 1));
+  if (isnan(threshold)) return fail(LLI8_ERR_THRESHOLD, "threshold is NaN");
+  if (T > 0) {
+    REQUIRE(X, "X");
+    REQUIRE(CA, "CA");
+    REQUIRE(SCA, "SCA");
+  }
+  REQUIRE(bitmap, "bitmap");
+  REQUIRE(idx, "idx");
+  REQUIRE(n_idx, "n_idx");
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  return enqueue_activation_split(X, T, K, (int)dtype, threshold, CA, SCA, bitmap, idx, n_idx, nullptr, s);
+}
+
+lli8_status_t lli8_int8_linear(const void* X, int64_t T, int64_t K, int64_t N, lli8_dtype_t dtype, const int8_t* CB,
+                               const float* SCB, const void* bias, float threshold, void* out,
+                               const lli8_workspace_t* ws, void* stream) {
+  TRY(check_dtype(dtype));
+  TRY(check_sizes(T, K, N));
+  if (isnan(threshold)) return fail(LLI8_ERR_THRESHOLD, "threshold is NaN");
+  REQUIRE(CB, "CB");
+  REQUIRE(SCB, "SCB");
+  OPTIONAL(bias, "bias");
+  if (ws == nullptr) return fail(LLI8_ERR_NULL, "workspace is NULL");
+  if (T > 0) {  // with T == 0 nothing of size T is read or written
+    REQUIRE(X, "X");
+    REQUIRE(out, "out");
+    REQUIRE(ws->CA, "ws->CA");
+    REQUIRE(ws->SCA, "ws->SCA");
+  }
+  REQUIRE(ws->bitmap, "ws->bitmap");
+  REQUIRE(ws->idx, "ws->idx");
+  REQUIRE(ws->n_idx, "ws->n_idx");
+  OPTIONAL(ws->acc, "ws->acc");
+  const bool outl = outliers_enabled(threshold);
+  if (outl && T > 0) {
+    const size_t need = lli8_scratch_bytes(T, K, dtype);
+    if (ws->scratch == nullptr || ws->scratch_bytes < need)
+      return fail(LLI8_ERR_WORKSPACE, "scratch needs %zu bytes, got %zu", need, ws->scratch ? ws->scratch_bytes : (size_t)0);
+    if (!aligned16(ws->scratch)) return fail(LLI8_ERR_ALIGN, "ws->scratch is not 16-byte aligned");
+  }
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  TRY(enqueue_activation_split(X, T, K, (int)dtype, threshold, ws->CA, ws->SCA, ws->bitmap, ws->idx, ws->n_idx,
+                               outl ? ws->scratch : nullptr, s));
+  lli8::LinearArgs a;
+  a.dt = (int)dtype;
+  a.CA = ws->CA;
+  a.CB = CB;
+  a.SCA = ws->SCA;
+  a.SCB = SCB;
+  a.bias = bias;
+  a.xo = outl ? ws->scratch : nullptr;
+  a.idx = ws->idx;
+  a.n_idx = ws->n_idx;
+  a.out = out;
+  a.acc = ws->acc;
+  a.T = T;
+  a.N = N;
+  a.K = K;
+  TRACED(s, "int8_gemm", lli8::launch_linear_gemm(a, s));
+  return LLI8_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,373 @@
+// int8 GEMM with the dequantisation, the 16-bit outlier product and the bias
+// fused into its epilogue, on gfx950 MFMA.
+//
+// The method ("Hugging Face integrates LLM.int8() ...", section "Core idea of
+// LLM.int8()"): the non-outlier part is an int8 x int8 product with int32
+// accumulation, dequantised with the row scale of the activation and the row
+// scale of the weight; the outlier columns are multiplied in 16-bit against
+// the weight recovered as (CB * SCB) / 127 (section "Integration into
+// transformers") and the two results are summed.
+//
+// Two kernels:
+//   * tile kernel: BM x BN output tile per 256-thread workgroup (2 x 2
+//     waves), K staged through LDS 64 bytes at a time, double buffered, with
+//     v_mfma_i32_32x32x32_i8.  The epilogue turns the int32 accumulators into
+//     fp32 in place (same 32x32 register layout), then runs the outlier
+//     columns through v_mfma_f32_32x32x16_{f16,bf16} on the same registers,
+//     then adds the bias and rounds once to the output dtype.
+//   * decode kernel (T <= 16): a streaming kernel; each workgroup owns 16
+//     output features and reads their int8 weight rows once with 16-byte
+//     loads, four waves splitting K, v_mfma_i32_16x16x64_i8.
+#include "lli8_device.h"
+#include "lli8_internal.h"
+
+namespace lli8 {
+
+constexpr int BK = 64;  // bytes of K staged per step (= int8 elements)
+
+// LDS address of 16-byte chunk c (0..3) of row r in a 64-byte-row tile.  The
+// XOR spreads the eight rows that one ds_read_b128 phase touches over all 32
+// banks, for both the row-wise writes and the MFMA-operand reads.
+__device__ __forceinline__ int lds_off(int r, int c) { return r * 64 + ((c ^ ((r >> 1) & 3)) << 4); }
+
+__device__ __forceinline__ u32x4 load16_i8(const int8_t* __restrict__ base, int64_t row, int64_t nrows,
+                                           int64_t K, int64_t k, bool vec) {
+  u32x4 z = {0u, 0u, 0u, 0u};
+  if (row >= nrows) return z;
+  const int8_t* p = base + row * K;
+  if (vec) {
+    if (k < K) z = *reinterpret_cast<const u32x4*>(p + k);
+    return z;
+  }
+  uint32_t w[4] = {0u, 0u, 0u, 0u};
+#pragma unroll
+  for (int b = 0; b < 16; ++b) {
+    const int64_t kk = k + b;
+    const uint32_t v = (kk < K) ? (uint32_t)(uint8_t)p[kk] : 0u;
+    w[b >> 2] |= v << (8 * (b & 3));
+  }
+  z[0] = w[0];
+  z[1] = w[1];
+  z[2] = w[2];
+  z[3] = w[3];
+  return z;
+}
+
+// Recovered weight value for the 16-bit product: dtype(fl32(fl32(cb*scb)/127)).
+template <int DT>
+__device__ __forceinline__ uint16_t recover_w(int8_t cb, float scb) {
+  const float p = (float)cb * scb;
+  return from_f32<DT>(p / 127.0f);
+}
+
+template <int DT>
+__device__ __forceinline__ v16f mfma16(const u32x4& a, const u32x4& b, const v16f& c) {
+  if constexpr (DT == DT_F16)
+    return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(v8h, a), __builtin_bit_cast(v8h, b), c, 0, 0, 0);
+  else
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(v8bf, a), __builtin_bit_cast(v8bf, b), c, 0, 0, 0);
+}
+
+// Tile index -> (tile_m, tile_n).  Workgroups are dispatched round-robin over
+// the eight XCDs; give each XCD a contiguous range of tiles, and walk that
+// range in groups of GM tile rows so neighbours share A rows and B columns in
+// their XCD's L2.
+template <int GM>
+__device__ __forceinline__ void tile_coords(int b, int tiles_m, int tiles_n, int& tm, int& tn) {
+  const int nb = tiles_m * tiles_n;
+  const int q = nb >> 3, rmd = nb & 7;
+  const int xcd = b & 7, loc = b >> 3;
+  const int t = xcd * q + min(xcd, rmd) + loc;
+  const int per_group = GM * tiles_n;
+  const int g = t / per_group;
+  const int first_m = g * GM;
+  const int gsz = min(tiles_m - first_m, GM);
+  const int in = t - g * per_group;
+  tm = first_m + in % gsz;
+  tn = in / gsz;
+}
+
+template <int DT, int BM, int BN, bool VEC>
+__global__ __launch_bounds__(256, 1) void linear_tile_kernel(
+    const int8_t* __restrict__ CA, const int8_t* __restrict__ CB, const float* __restrict__ SCA,
+    const float* __restrict__ SCB, const uint16_t* __restrict__ bias, const uint16_t* __restrict__ xo,
+    const int32_t* __restrict__ idx, const int32_t* __restrict__ n_idx_p, uint16_t* __restrict__ out,
+    int32_t* __restrict__ acc_out, int T, int N, int K, int tiles_m, int tiles_n) {
+  constexpr int WM = BM / 2, WN = BN / 2;
+  constexpr int FM = WM / 32, FN = WN / 32;
+  constexpr int LA = BM * 4 / 256, LB = BN * 4 / 256;  // 16-byte chunks per thread per step
+  __shared__ __attribute__((aligned(16))) int8_t sA[2][BM * BK];
+  __shared__ __attribute__((aligned(16))) int8_t sB[2][BN * BK];
+
+  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+  const int wm = wid >> 1, wn = wid & 1;
+  int tm, tn;
+  tile_coords<8>(blockIdx.x, tiles_m, tiles_n, tm, tn);
+  const int64_t m0 = (int64_t)tm * BM, n0 = (int64_t)tn * BN;
+  const int n_idx = *n_idx_p;
+
+  v16i acc[FM][FN];
+#pragma unroll
+  for (int i = 0; i < FM; ++i)
+#pragma unroll
+    for (int j = 0; j < FN; ++j) acc[i][j] = (v16i){0};
+
+  u32x4 ra[LA], rb[LB];
+  auto gload = [&](int kt) {
+    const int64_t k0 = (int64_t)kt * BK;
+#pragma unroll
+    for (int i = 0; i < LA; ++i) {
+      const int q = tid + 256 * i, r = q >> 2, c = q & 3;
+      ra[i] = load16_i8(CA, m0 + r, T, K, k0 + c * 16, VEC);
+    }
+#pragma unroll
+    for (int i = 0; i < LB; ++i) {
+      const int q = tid + 256 * i, r = q >> 2, c = q & 3;
+      rb[i] = load16_i8(CB, n0 + r, N, K, k0 + c * 16, VEC);
+    }
+  };
+  auto lstore = [&](int buf) {
+#pragma unroll
+    for (int i = 0; i < LA; ++i) {
+      const int q = tid + 256 * i, r = q >> 2, c = q & 3;
+      *reinterpret_cast<u32x4*>(&sA[buf][lds_off(r, c)]) = ra[i];
+    }
+#pragma unroll
+    for (int i = 0; i < LB; ++i) {
+      const int q = tid + 256 * i, r = q >> 2, c = q & 3;
+      *reinterpret_cast<u32x4*>(&sB[buf][lds_off(r, c)]) = rb[i];
+    }
+  };
+
+  const int nk = (K + BK - 1) / BK;
+  gload(0);
+  lstore(0);
+  __syncthreads();
+  for (int kt = 0; kt < nk; ++kt) {
+    const int cur = kt & 1;
+    if (kt + 1 < nk) gload(kt + 1);
+#pragma unroll
+    for (int s = 0; s < 2; ++s) {
+      const int c = 2 * s + (lane >> 5);
+      v4i a[FM], b[FN];
+#pragma unroll
+      for (int i = 0; i < FM; ++i)
+        a[i] = *reinterpret_cast<const v4i*>(&sA[cur][lds_off(wm * WM + i * 32 + (lane & 31), c)]);
+#pragma unroll
+      for (int j = 0; j < FN; ++j)
+        b[j] = *reinterpret_cast<const v4i*>(&sB[cur][lds_off(wn * WN + j * 32 + (lane & 31), c)]);
+#pragma unroll
+      for (int i = 0; i < FM; ++i)
+#pragma unroll
+        for (int j = 0; j < FN; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(a[i], b[j], acc[i][j], 0, 0, 0);
+    }
+    if (kt + 1 < nk) lstore(cur ^ 1);
+    __syncthreads();
+  }
+
+  // ---- epilogue.  32x32 accumulator layout: lane holds column (lane & 31),
+  // register r holds row 8 * (r / 4) + 4 * (lane / 32) + r % 4.
+  const int64_t rbase = m0 + wm * WM + 4 * (lane >> 5);
+  const int64_t cbase = n0 + wn * WN + (lane & 31);
+  if (acc_out != nullptr) {
+#pragma unroll
+    for (int i = 0; i < FM; ++i) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int64_t row = rbase + i * 32 + 8 * (r >> 2) + (r & 3);
+        if (row >= T) continue;
+        int32_t* arow = acc_out + row * N + cbase;
+#pragma unroll
+        for (int j = 0; j < FN; ++j)
+          if (cbase + j * 32 < N) arow[j * 32] = acc[i][j][r];
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  }
+  // Dequantise in place: the fp32 value reuses the int32 accumulator's
+  // registers (the f32 and i32 32x32 MFMAs share one register layout).
+  float sb[FN];
+#pragma unroll
+  for (int j = 0; j < FN; ++j) {
+    const int64_t col = cbase + j * 32;
+    sb[j] = (col < N) ? SCB[col] * (1.0f / 16129.0f) : 0.0f;
+  }
+#pragma unroll
+  for (int i = 0; i < FM; ++i) {
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int64_t row = rbase + i * 32 + 8 * (r >> 2) + (r & 3);
+      const float sa = (row < T) ? SCA[row] : 0.0f;
+#pragma unroll
+      for (int j = 0; j < FN; ++j)
+        acc[i][j][r] = __float_as_int((float)acc[i][j][r] * (sa * sb[j]));
+    }
+    __builtin_amdgcn_sched_barrier(0);  // keep the per-row loads of one strip at a time
+  }
+
+  // 16-bit outlier product, 32 outlier columns per step, LDS reused.
+  const int n_chunks = (n_idx + 31) >> 5;
+  int8_t* oA = &sA[0][0];  // [BM][32] 16-bit values, 64-byte rows
+  int8_t* oB = &sB[0][0];  // [BN][32]
+  for (int ch = 0; ch < n_chunks; ++ch) {
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < LA; ++i) {
+      const int q = tid + 256 * i, r = q >> 2, c = q & 3;
+      u32x4 v = {0u, 0u, 0u, 0u};
+      if (m0 + r < T) v = *reinterpret_cast<const u32x4*>(xo + (((int64_t)ch * T + m0 + r) * 32 + c * 8));
+      *reinterpret_cast<u32x4*>(oA + lds_off(r, c)) = v;
+    }
+    {
+      const int j = tid & 31;
+      const int p = ch * 32 + j;
+      const bool valid = p < n_idx;
+      const int64_t col = valid ? idx[p] : 0;
+      for (int rr = tid >> 5; rr < BN; rr += 8) {
+        const int64_t gn = n0 + rr;
+        uint16_t w = 0;
+        if (valid && gn < N) w = recover_w<DT>(CB[gn * K + col], SCB[gn]);
+        *reinterpret_cast<uint16_t*>(oB + lds_off(rr, j >> 3) + (j & 7) * 2) = w;
+      }
+    }
+    __syncthreads();
+#pragma unroll
+    for (int s = 0; s < 2; ++s) {
+      const int c = 2 * s + (lane >> 5);
+      u32x4 a[FM], b[FN];
+#pragma unroll
+      for (int i = 0; i < FM; ++i) a[i] = *reinterpret_cast<const u32x4*>(oA + lds_off(wm * WM + i * 32 + (lane & 31), c));
+#pragma unroll
+      for (int j = 0; j < FN; ++j) b[j] = *reinterpret_cast<const u32x4*>(oB + lds_off(wn * WN + j * 32 + (lane & 31), c));
+#pragma unroll
+      for (int i = 0; i < FM; ++i)
+#pragma unroll
+        for (int j = 0; j < FN; ++j)
+          acc[i][j] = __builtin_bit_cast(v16i, mfma16<DT>(a[i], b[j], __builtin_bit_cast(v16f, acc[i][j])));
+    }
+  }
+
+  // bias, one rounding to the output dtype, store.
+  float bv[FN];
+#pragma unroll
+  for (int j = 0; j < FN; ++j) {
+    const int64_t col = cbase + j * 32;
+    bv[j] = (bias != nullptr && col < N) ? to_f32<DT>(bias[col]) : 0.0f;
+  }
+#pragma unroll
+  for (int i = 0; i < FM; ++i) {
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int64_t row = rbase + i * 32 + 8 * (r >> 2) + (r & 3);
+      if (row >= T) continue;
+      uint16_t* orow = out + row * N + cbase;
+#pragma unroll
+      for (int j = 0; j < FN; ++j)
+        if (cbase + j * 32 < N) orow[j * 32] = from_f32<DT>(__int_as_float(acc[i][j][r]) + bv[j]);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+  }
+}
+
+// ---------------------------------------------------------------- decode ----
+// T <= 16, K % 16 == 0.  Workgroup = 16 output features; wave w takes the
+// 256-byte K slices w, w + 4, ...; lane (n, g) = (lane % 16, lane / 16) loads
+// 64 contiguous bytes of weight row n and the matching activation bytes, which
+// feed four 16x16x64 MFMAs (A and B use the same K permutation, so the dot
+// products are exact).  Partial int32 tiles are summed through LDS in a fixed
+// order (deterministic).
+template <int DT>
+__global__ __launch_bounds__(256) void linear_decode_kernel(
+    const int8_t* __restrict__ CA, const int8_t* __restrict__ CB, const float* __restrict__ SCA,
+    const float* __restrict__ SCB, const uint16_t* __restrict__ bias, const uint16_t* __restrict__ xo,
+    const int32_t* __restrict__ idx, const int32_t* __restrict__ n_idx_p, uint16_t* __restrict__ out,
+    int32_t* __restrict__ acc_out, int T, int N, int K) {
+  __shared__ v4i red[3][64];
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int64_t n0 = (int64_t)blockIdx.x * 16;
+  const int nr = lane & 15, g = lane >> 4;
+  const int64_t n = n0 + nr;
+  const int nss = (K + 255) >> 8;
+  v4i acc = {0, 0, 0, 0};
+  const int8_t* brow = CB + n * (int64_t)K;
+  const int8_t* arow = CA + (int64_t)nr * K;
+  for (int s = w; s < nss; s += 4) {
+    const int64_t kb = (int64_t)s * 256 + g * 64;
+    u32x4 a[4], b[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int64_t k = kb + 16 * u;
+      b[u] = (n < N && k < K) ? __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(brow + k))
+                              : (u32x4){0u, 0u, 0u, 0u};
+      a[u] = (nr < T && k < K) ? *reinterpret_cast<const u32x4*>(arow + k) : (u32x4){0u, 0u, 0u, 0u};
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+      acc = __builtin_amdgcn_mfma_i32_16x16x64_i8(__builtin_bit_cast(v4i, a[u]), __builtin_bit_cast(v4i, b[u]),
+                                                  acc, 0, 0, 0);
+  }
+  if (w > 0) red[w - 1][lane] = acc;
+  __syncthreads();
+  if (w != 0) return;
+  acc += red[0][lane];
+  acc += red[1][lane];
+  acc += red[2][lane];
+
+  // 16x16 accumulator layout: lane holds column lane % 16, rows 4 * (lane / 16) + r.
+  const int n_idx = *n_idx_p;
+  const int64_t col = n0 + (lane & 15);
+  if (col >= N) return;
+  const float scb = SCB[col];
+  const float bv = (bias != nullptr) ? to_f32<DT>(bias[col]) : 0.0f;
+  float o[4] = {0.f, 0.f, 0.f, 0.f};
+  for (int p = 0; p < n_idx; ++p) {
+    const float wv = to_f32<DT>(recover_w<DT>(CB[col * K + idx[p]], scb));
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int t = 4 * (lane >> 4) + r;
+      if (t < T) o[r] += to_f32<DT>(xo[((int64_t)(p >> 5) * T + t) * 32 + (p & 31)]) * wv;
+    }
+  }
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    const int t = 4 * (lane >> 4) + r;
+    if (t >= T) continue;
+    if (acc_out != nullptr) acc_out[(int64_t)t * N + col] = acc[r];
+    const float d = (float)acc[r] * (SCA[t] * (scb * (1.0f / 16129.0f)));
+    out[(int64_t)t * N + col] = from_f32<DT>(d + o[r] + bv);
+  }
+}
+
+template <int DT, int BM, int BN>
+static hipError_t launch_tile(const LinearArgs& a, hipStream_t s) {
+  const int tiles_m = (int)((a.T + BM - 1) / BM), tiles_n = (int)((a.N + BN - 1) / BN);
+  const int nb = tiles_m * tiles_n;
+  const bool vec = (a.K % 16) == 0;
+  auto k = vec ? linear_tile_kernel<DT, BM, BN, true> : linear_tile_kernel<DT, BM, BN, false>;
+  k<<<dim3(nb), dim3(256), 0, s>>>(a.CA, a.CB, a.SCA, a.SCB, static_cast<const uint16_t*>(a.bias),
+                                   static_cast<const uint16_t*>(a.xo), a.idx, a.n_idx,
+                                   static_cast<uint16_t*>(a.out), a.acc, (int)a.T, (int)a.N, (int)a.K,
+                                   tiles_m, tiles_n);
+  return hipGetLastError();
+}
+
+template <int DT>
+static hipError_t launch_linear_t(const LinearArgs& a, hipStream_t s) {
+  if (a.T <= 16 && (a.K % 16) == 0) {
+    const int nb = (int)((a.N + 15) / 16);
+    linear_decode_kernel<DT><<<dim3(nb), dim3(256), 0, s>>>(
+        a.CA, a.CB, a.SCA, a.SCB, static_cast<const uint16_t*>(a.bias), static_cast<const uint16_t*>(a.xo),
+        a.idx, a.n_idx, static_cast<uint16_t*>(a.out), a.acc, (int)a.T, (int)a.N, (int)a.K);
+    return hipGetLastError();
+  }
+  if (a.T >= 512 && a.N >= 512) return launch_tile<DT, 256, 256>(a, s);
+  return launch_tile<DT, 128, 128>(a, s);
+}
+
+hipError_t launch_linear_gemm(const LinearArgs& a, hipStream_t s) {
+  if (a.T <= 0) return hipSuccess;
+  return a.dt == DT_F16 ? launch_linear_t<DT_F16>(a, s) : launch_linear_t<DT_BF16>(a, s);
+}
+
+}  // namespace lli8

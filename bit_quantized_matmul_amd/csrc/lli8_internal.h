@@ -1,0 +1,38 @@
+// Host-side launchers of the lli8 kernels (internal to the library).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace lli8 {
+
+hipError_t launch_fill_u32(uint32_t* p, int64_t n, uint32_t v, hipStream_t s);
+
+hipError_t launch_quant_weight(int dt, const void* W, int64_t N, int64_t K, int8_t* CB,
+                               float* SCB, hipStream_t s);
+
+hipError_t launch_scan_outliers(int dt, const void* X, int64_t T, int64_t K, float tau,
+                                uint32_t* bitmap, hipStream_t s);
+
+hipError_t launch_quant_act(int dt, const void* X, int64_t T, int64_t K, const uint32_t* bitmap,
+                            int8_t* CA, float* SCA, int32_t* idx, int32_t* n_idx, void* xo,
+                            hipStream_t s);
+
+struct LinearArgs {
+  int dt;
+  const int8_t* CA;
+  const int8_t* CB;
+  const float* SCA;
+  const float* SCB;
+  const void* bias;      // may be null
+  const void* xo;        // gathered outlier columns, chunk-major [ceil(n/32)][T][32]
+  const int32_t* idx;
+  const int32_t* n_idx;  // device
+  void* out;
+  int32_t* acc;          // may be null
+  int64_t T, N, K;
+};
+
+hipError_t launch_linear_gemm(const LinearArgs& a, hipStream_t s);
+
+}  // namespace lli8

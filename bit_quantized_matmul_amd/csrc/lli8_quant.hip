@@ -1,0 +1,332 @@
+// Quantisation kernels of the LLM.int8() linear on gfx950:
+//   * outlier-column scan of the activation (bitmap built with atomic OR),
+//   * row-wise absmax quantisation of the activation with the outlier columns
+//     left out (codes, scales, ascending outlier index list, gathered outlier
+//     columns for the 16-bit product),
+//   * row-wise absmax quantisation of the weight.
+// The method: "Hugging Face integrates LLM.int8() ...", sections "Core idea of
+// LLM.int8()" (steps 1-2) and "Quantization mechanics" (absmax bullet).
+// All three are HBM-bound streaming kernels: one wave owns a contiguous
+// stretch of a row and reads it with 16-byte loads.
+#include "lli8_device.h"
+#include "lli8_internal.h"
+
+namespace lli8 {
+
+// ---------------------------------------------------------------- fill ----
+__global__ void fill_u32_kernel(uint32_t* __restrict__ p, int64_t n, uint32_t v) {
+  int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < n) p[i] = v;
+}
+
+hipError_t launch_fill_u32(uint32_t* p, int64_t n, uint32_t v, hipStream_t s) {
+  if (n <= 0) return hipSuccess;
+  const int64_t blocks = (n + 255) / 256;
+  fill_u32_kernel<<<dim3((unsigned)blocks), dim3(256), 0, s>>>(p, n, v);
+  return hipGetLastError();
+}
+
+// --------------------------------------------------------- outlier scan ----
+// Column c is an outlier when some row has |X[t, c]| > tau.  Lane owns one
+// 16-byte chunk (8 columns) and walks rows; four lanes make one bitmap word,
+// which is OR-ed into the global bitmap only when non-zero (outlier columns
+// are rare, so atomics are rare).  Requires K % 8 == 0.
+template <int DT>
+__global__ __launch_bounds__(256) void scan_outliers_vec_kernel(
+    const uint16_t* __restrict__ X, int64_t T, int64_t K, float tau,
+    uint32_t* __restrict__ bitmap, int rows_per_block) {
+  const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+  const int64_t nch = K >> 3;
+  const int64_t c = (int64_t)blockIdx.x * 64 + lane;
+  const int64_t r0 = (int64_t)blockIdx.y * rows_per_block;
+  const int64_t r1 = min(T, r0 + rows_per_block);
+  uint32_t flags = 0;
+  if (c < nch) {
+    const u32x4* p = reinterpret_cast<const u32x4*>(X) + c;
+    const int64_t stride = nch;  // chunks per row
+#pragma unroll 8
+    for (int64_t r = r0 + wid; r < r1; r += 4) {
+      const u32x4 v = p[r * stride];  // cached: the quantiser reads X again
+#pragma unroll
+      for (int e = 0; e < 8; ++e)
+        flags |= (fabsf(to_f32<DT>(half_bits(v, e))) > tau ? 1u : 0u) << e;
+    }
+  }
+  uint32_t w = flags << ((lane & 3) * 8);
+  w |= __shfl_xor(w, 1, WAVE);
+  w |= __shfl_xor(w, 2, WAVE);
+  if ((lane & 3) == 0 && c < nch && w != 0u) atomicOr(bitmap + (c >> 2), w);
+}
+
+// Any K: one thread per column, 64 columns per wave form two bitmap words.
+template <int DT>
+__global__ __launch_bounds__(256) void scan_outliers_any_kernel(
+    const uint16_t* __restrict__ X, int64_t T, int64_t K, float tau,
+    uint32_t* __restrict__ bitmap, int rows_per_block) {
+  const int lane = threadIdx.x & 63;
+  const int64_t col = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const int64_t r0 = (int64_t)blockIdx.y * rows_per_block;
+  const int64_t r1 = min(T, r0 + rows_per_block);
+  bool flag = false;
+  if (col < K)
+    for (int64_t r = r0; r < r1; ++r) flag |= fabsf(to_f32<DT>(X[r * K + col])) > tau;
+  const uint64_t m = __ballot(flag);
+  const int64_t col0 = col - lane;  // multiple of 64
+  if (lane == 0) {
+    const uint32_t lo = (uint32_t)m, hi = (uint32_t)(m >> 32);
+    if (lo) atomicOr(bitmap + (col0 >> 5), lo);
+    if (hi) atomicOr(bitmap + (col0 >> 5) + 1, hi);
+  }
+}
+
+hipError_t launch_scan_outliers(int dt, const void* X, int64_t T, int64_t K, float tau,
+                                uint32_t* bitmap, hipStream_t s) {
+  if (T <= 0) return hipSuccess;
+  const uint16_t* x = static_cast<const uint16_t*>(X);
+  if ((K & 7) == 0) {
+    const int64_t gx = (K / 8 + 63) / 64;
+    // Aim for >= ~2048 workgroups on big inputs, at most 64 rows per workgroup.
+    int rows = 64;
+    while (rows > 4 && gx * ((T + rows - 1) / rows) < 2048) rows >>= 1;
+    const int64_t gy = (T + rows - 1) / rows;
+    dim3 grid((unsigned)gx, (unsigned)gy);
+    if (dt == DT_F16)
+      scan_outliers_vec_kernel<DT_F16><<<grid, 256, 0, s>>>(x, T, K, tau, bitmap, rows);
+    else
+      scan_outliers_vec_kernel<DT_BF16><<<grid, 256, 0, s>>>(x, T, K, tau, bitmap, rows);
+  } else {
+    const int64_t gx = (K + 255) / 256;
+    const int rows = 64;
+    dim3 grid((unsigned)gx, (unsigned)((T + rows - 1) / rows));
+    if (dt == DT_F16)
+      scan_outliers_any_kernel<DT_F16><<<grid, 256, 0, s>>>(x, T, K, tau, bitmap, rows);
+    else
+      scan_outliers_any_kernel<DT_BF16><<<grid, 256, 0, s>>>(x, T, K, tau, bitmap, rows);
+  }
+  return hipGetLastError();
+}
+
+// ------------------------------------------------------- row quantisers ----
+// Shared prologue of the activation quantiser: the bitmap goes to LDS with an
+// exclusive prefix count per word, so every column knows its rank among the
+// outlier columns.  Block 0 also writes the ascending index list and count.
+// LDS: words[W], prefix[W].  Returns the number of outlier columns.
+__device__ int load_bitmap_prefix(const uint32_t* __restrict__ bitmap, int64_t W,
+                                  uint32_t* words, uint32_t* prefix,
+                                  int32_t* __restrict__ idx, int32_t* __restrict__ n_idx) {
+  for (int64_t w = threadIdx.x; w < W; w += blockDim.x) words[w] = bitmap[w];
+  __syncthreads();
+  if (threadIdx.x < 64) {
+    const int lane = threadIdx.x;
+    const int64_t seg = (W + 63) / 64;
+    const int64_t w0 = lane * seg, w1 = min(W, w0 + seg);
+    int cnt = 0;
+    for (int64_t w = w0; w < w1; ++w) cnt += __popc(words[w]);
+    int run = wave_incl_scan(cnt) - cnt;
+    for (int64_t w = w0; w < w1; ++w) {
+      prefix[w] = (uint32_t)run;
+      run += __popc(words[w]);
+    }
+  }
+  __syncthreads();
+  const int total = (W > 0) ? (int)(prefix[W - 1] + __popc(words[W - 1])) : 0;
+  if (blockIdx.x == 0) {
+    for (int64_t w = threadIdx.x; w < W; w += blockDim.x) {
+      uint32_t m = words[w];
+      int pos = (int)prefix[w];
+      while (m) {
+        const int b = __builtin_ctz(m);
+        idx[pos++] = (int32_t)(w * 32 + b);
+        m &= m - 1u;
+      }
+    }
+    if (threadIdx.x == 0) *n_idx = total;
+  }
+  return total;
+}
+
+// Gathered outlier columns of X: chunk-major [ceil(n/32)][T][32] of 16-bit
+// values, zero beyond n, so the 16-bit product can stream 64-byte rows.
+__device__ __forceinline__ int64_t xo_offset(int p, int64_t row, int64_t T) {
+  return ((int64_t)(p >> 5) * T + row) * 32 + (p & 31);
+}
+
+__device__ __forceinline__ void xo_zero_pad(uint16_t* __restrict__ xo, int total, int64_t row,
+                                            int64_t T, int lane) {
+  const int npad = (total + 31) & ~31;
+  for (int p = total + lane; p < npad; p += WAVE) xo[xo_offset(p, row, T)] = 0;
+}
+
+// One wave per row; the row stays in registers (MAXC 16-byte chunks per lane),
+// so HBM sees it once.  Requires K % 8 == 0 and K <= 512 * MAXC.
+// EXCL: activation mode (outlier columns excluded, index list, gather).
+template <int DT, bool EXCL, int MAXC>
+__global__ __launch_bounds__(256) void quant_rows_reg_kernel(
+    const uint16_t* __restrict__ src, int64_t R, int64_t K, int8_t* __restrict__ codes,
+    float* __restrict__ scales, const uint32_t* __restrict__ bitmap,
+    int32_t* __restrict__ idx, int32_t* __restrict__ n_idx, uint16_t* __restrict__ xo) {
+  extern __shared__ uint32_t lds[];
+  const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+  const int64_t W = (K + 31) >> 5;
+  int total = 0;
+  if constexpr (EXCL) total = load_bitmap_prefix(bitmap, W, lds, lds + W, idx, n_idx);
+  const uint32_t* words = lds;
+  const uint32_t* prefix = lds + W;
+
+  const int64_t row = (int64_t)blockIdx.x * 4 + wid;
+  if (row >= R) return;
+  const int64_t nch = K >> 3;
+  const u32x4* rp = reinterpret_cast<const u32x4*>(src + row * K);
+  u32x4 v[MAXC];
+#pragma unroll
+  for (int i = 0; i < MAXC; ++i) {
+    const int64_t c = lane + (int64_t)i * WAVE;
+    if (c < nch) v[i] = __builtin_nontemporal_load(rp + c);
+  }
+  float m = 0.0f;
+#pragma unroll
+  for (int i = 0; i < MAXC; ++i) {
+    const int64_t c = lane + (int64_t)i * WAVE;
+    if (c < nch) {
+      uint32_t out_bits = 0;
+      if constexpr (EXCL) out_bits = (words[c >> 2] >> ((c & 3) * 8)) & 0xFFu;
+#pragma unroll
+      for (int e = 0; e < 8; ++e)
+        if (!((out_bits >> e) & 1u)) m = fmaxf(m, fabsf(to_f32<DT>(half_bits(v[i], e))));
+    }
+  }
+  m = wave_max(m);
+  const float s = (m > 0.0f) ? 127.0f / m : 0.0f;
+  u32x2* cp = reinterpret_cast<u32x2*>(codes + row * K);
+#pragma unroll
+  for (int i = 0; i < MAXC; ++i) {
+    const int64_t c = lane + (int64_t)i * WAVE;
+    if (c < nch) {
+      uint32_t out_bits = 0;
+      if constexpr (EXCL) out_bits = (words[c >> 2] >> ((c & 3) * 8)) & 0xFFu;
+      uint32_t lo = 0, hi = 0;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const uint32_t h = half_bits(v[i], e);
+        int q = 0;
+        if (!((out_bits >> e) & 1u) && m > 0.0f) q = quant_code(to_f32<DT>(h), s);
+        const uint32_t b = (uint32_t)(q & 0xFF);
+        if (e < 4) lo |= b << (8 * e); else hi |= b << (8 * (e - 4));
+      }
+      u32x2 pk;
+      pk[0] = lo;
+      pk[1] = hi;
+      cp[c] = pk;
+      if constexpr (EXCL) {
+        if (out_bits && xo != nullptr) {
+          const uint32_t word = words[c >> 2];
+          const int base = (int)prefix[c >> 2];
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            if ((out_bits >> e) & 1u) {
+              const int bit = (int)((c & 3) * 8 + e);
+              const int p = base + __popc(word & ((1u << bit) - 1u));
+              xo[xo_offset(p, row, R)] = (uint16_t)half_bits(v[i], e);
+            }
+          }
+        }
+      }
+    }
+  }
+  if (lane == 0) scales[row] = m;
+  if constexpr (EXCL) {
+    if (xo != nullptr) xo_zero_pad(xo, total, row, R, lane);
+  }
+}
+
+// Any K (and K beyond the register budget): two passes over the row, the
+// second served from cache.  One wave per row.
+template <int DT, bool EXCL>
+__global__ __launch_bounds__(256) void quant_rows_any_kernel(
+    const uint16_t* __restrict__ src, int64_t R, int64_t K, int8_t* __restrict__ codes,
+    float* __restrict__ scales, const uint32_t* __restrict__ bitmap,
+    int32_t* __restrict__ idx, int32_t* __restrict__ n_idx, uint16_t* __restrict__ xo) {
+  extern __shared__ uint32_t lds[];
+  const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+  const int64_t W = (K + 31) >> 5;
+  int total = 0;
+  if constexpr (EXCL) total = load_bitmap_prefix(bitmap, W, lds, lds + W, idx, n_idx);
+  const uint32_t* words = lds;
+  const uint32_t* prefix = lds + W;
+
+  const int64_t row = (int64_t)blockIdx.x * 4 + wid;
+  if (row >= R) return;
+  const uint16_t* rp = src + row * K;
+  float m = 0.0f;
+  for (int64_t k = lane; k < K; k += WAVE) {
+    bool out = false;
+    if constexpr (EXCL) out = (words[k >> 5] >> (k & 31)) & 1u;
+    if (!out) m = fmaxf(m, fabsf(to_f32<DT>(rp[k])));
+  }
+  m = wave_max(m);
+  const float s = (m > 0.0f) ? 127.0f / m : 0.0f;
+  int8_t* cp = codes + row * K;
+  for (int64_t k = lane; k < K; k += WAVE) {
+    const uint32_t h = rp[k];
+    bool out = false;
+    if constexpr (EXCL) out = (words[k >> 5] >> (k & 31)) & 1u;
+    int q = 0;
+    if (!out && m > 0.0f) q = quant_code(to_f32<DT>(h), s);
+    cp[k] = (int8_t)q;
+    if constexpr (EXCL) {
+      if (out && xo != nullptr) {
+        const uint32_t word = words[k >> 5];
+        const int p = (int)prefix[k >> 5] + __popc(word & ((1u << (k & 31)) - 1u));
+        xo[xo_offset(p, row, R)] = (uint16_t)h;
+      }
+    }
+  }
+  if (lane == 0) scales[row] = m;
+  if constexpr (EXCL) {
+    if (xo != nullptr) xo_zero_pad(xo, total, row, R, lane);
+  }
+}
+
+template <int DT, bool EXCL>
+static hipError_t launch_quant_rows_t(const uint16_t* src, int64_t R, int64_t K, int8_t* codes,
+                                      float* scales, const uint32_t* bitmap, int32_t* idx,
+                                      int32_t* n_idx, uint16_t* xo, hipStream_t s) {
+  // Activation mode launches at least one block, so that block 0 writes the
+  // index list and count even for T == 0.
+  const int64_t nb4 = (R + 3) / 4;
+  const int64_t blocks = (EXCL && nb4 < 1) ? 1 : nb4;
+  if (blocks == 0) return hipSuccess;
+  const size_t lds = EXCL ? (size_t)2 * ((K + 31) / 32) * sizeof(uint32_t) : 0;
+  dim3 grid((unsigned)blocks), block(256);
+  if ((K & 7) == 0 && K <= 512 * 2)
+    quant_rows_reg_kernel<DT, EXCL, 2><<<grid, block, lds, s>>>(src, R, K, codes, scales, bitmap, idx, n_idx, xo);
+  else if ((K & 7) == 0 && K <= 512 * 8)
+    quant_rows_reg_kernel<DT, EXCL, 8><<<grid, block, lds, s>>>(src, R, K, codes, scales, bitmap, idx, n_idx, xo);
+  else if ((K & 7) == 0 && K <= 512 * 16)
+    quant_rows_reg_kernel<DT, EXCL, 16><<<grid, block, lds, s>>>(src, R, K, codes, scales, bitmap, idx, n_idx, xo);
+  else if ((K & 7) == 0 && K <= 512 * 24)
+    quant_rows_reg_kernel<DT, EXCL, 24><<<grid, block, lds, s>>>(src, R, K, codes, scales, bitmap, idx, n_idx, xo);
+  else
+    quant_rows_any_kernel<DT, EXCL><<<grid, block, lds, s>>>(src, R, K, codes, scales, bitmap, idx, n_idx, xo);
+  return hipGetLastError();
+}
+
+hipError_t launch_quant_weight(int dt, const void* W, int64_t N, int64_t K, int8_t* CB, float* SCB,
+                               hipStream_t s) {
+  const uint16_t* w = static_cast<const uint16_t*>(W);
+  if (dt == DT_F16)
+    return launch_quant_rows_t<DT_F16, false>(w, N, K, CB, SCB, nullptr, nullptr, nullptr, nullptr, s);
+  return launch_quant_rows_t<DT_BF16, false>(w, N, K, CB, SCB, nullptr, nullptr, nullptr, nullptr, s);
+}
+
+hipError_t launch_quant_act(int dt, const void* X, int64_t T, int64_t K, const uint32_t* bitmap,
+                            int8_t* CA, float* SCA, int32_t* idx, int32_t* n_idx, void* xo,
+                            hipStream_t s) {
+  const uint16_t* x = static_cast<const uint16_t*>(X);
+  uint16_t* g = static_cast<uint16_t*>(xo);
+  if (dt == DT_F16)
+    return launch_quant_rows_t<DT_F16, true>(x, T, K, CA, SCA, bitmap, idx, n_idx, g, s);
+  return launch_quant_rows_t<DT_BF16, true>(x, T, K, CA, SCA, bitmap, idx, n_idx, g, s);
+}
+
+}  // namespace lli8

@@ -1,0 +1,175 @@
+/*
+ * lli8 -- the LLM.int8() mixed-precision decomposition linear (forward) on
+ * AMD Instinct MI355X (gfx950).
+ *
+ * The operation, as the pages define it:
+ *   - "Hugging Face integrates LLM.int8() 8-bit matrix multiplication into
+ *     Transformers and Accelerate", section "Core idea of LLM.int8()":
+ *     (1) feature columns of the activation holding a value whose magnitude
+ *     exceeds a threshold are split off; (2) they are multiplied in 16-bit,
+ *     while the rest is quantised to int8 with vector-wise scales (one per
+ *     activation row, one per weight output row) and multiplied in int8;
+ *     (3) the int8 result is dequantised and summed with the 16-bit result.
+ *   - same page, section "Quantization mechanics": absmax quantisation
+ *     scales a vector by 127 / absmax and rounds, giving codes in [-127, 127].
+ *   - same page, section "Integration into transformers": the int8 weight CB
+ *     and its scale SCB recover the weight as (CB * SCB) / 127.
+ *   - "Class Linear8bitLt", __init__ Args: with has_fp16_weights=False the
+ *     weight is quantised once when the module is placed on the device; with
+ *     True it is quantised in every forward.  The threshold acts on the
+ *     activation columns.
+ *
+ * Conventions shared by every entry point
+ *   - Every tensor pointer is a DEVICE pointer to a caller-owned, contiguous,
+ *     row-major buffer.  The library allocates no device memory and keeps no
+ *     per-call state; all work is enqueued asynchronously on `stream`
+ *     (a hipStream_t; NULL means the default stream).  No call synchronises
+ *     the host.
+ *   - X, W, bias and out share one 16-bit dtype (fp16 or bf16).  Codes (CA,
+ *     CB) are int8 in [-127, 127]; scales (SCA, SCB) are fp32 and hold the
+ *     row absmax itself; the dequantisation factor is SCA * SCB / 127^2.
+ *   - Rounding of codes: round(fl32(x * fl32(127 / absmax))), halves away
+ *     from zero.  A row whose absmax is 0 gets scale 0 and all-zero codes.
+ *   - threshold: column c is an outlier when some |X[t, c]| > threshold
+ *     (strict, compared in fp32).  threshold <= 0 or +inf: no outlier
+ *     columns (plain vector-wise int8).  NaN: LLI8_ERR_THRESHOLD.
+ *   - Arguments are validated before anything is enqueued; on a validation
+ *     error nothing is written.  A launch failure returns LLI8_ERR_HIP and
+ *     lli8_last_error() gives the runtime's message.  No C++ exception
+ *     crosses this interface.  Sizes are int64_t; 0 <= T, 1 <= K, N;
+ *     K <= 133144 keeps every int32 accumulator exact.
+ *   - Device pointers must be 16-byte aligned (LLI8_ERR_ALIGN otherwise).
+ *     With T == 0, the buffers whose size is a multiple of T (X, CA, SCA,
+ *     out, acc) may be NULL.
+ */
+#ifndef LLI8_H
+#define LLI8_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum { LLI8_F16 = 0, LLI8_BF16 = 1 } lli8_dtype_t;
+
+typedef enum {
+  LLI8_OK = 0,
+  LLI8_ERR_NULL = 1,        /* a required pointer is NULL                        */
+  LLI8_ERR_SHAPE = 2,       /* T < 0, K < 1 or N < 1                             */
+  LLI8_ERR_DTYPE = 3,       /* dtype is not LLI8_F16 / LLI8_BF16                 */
+  LLI8_ERR_ALIGN = 4,       /* a device pointer is not 16-byte aligned           */
+  LLI8_ERR_THRESHOLD = 5,   /* threshold is NaN                                  */
+  LLI8_ERR_UNSUPPORTED = 6, /* K above 133144 (int32 accumulator headroom)       */
+  LLI8_ERR_HIP = 7,         /* the HIP runtime reported an error                 */
+  LLI8_ERR_WORKSPACE = 8    /* scratch buffer missing or smaller than required   */
+} lli8_status_t;
+
+/*
+ * Weight quantisation (per output row), "Core idea of LLM.int8()" step 2 and
+ * "Integration into transformers" (CB, SCB, recovery (CB * SCB) / 127).
+ *   W   [N, K] fp16/bf16 (read)
+ *   CB  [N, K] int8 (written): round(fl32(W * fl32(127 / SCB[n])))
+ *   SCB [N] fp32 (written): max_k |W[n, k]|
+ * Called once at placement (has_fp16_weights=False) or before every forward
+ * (has_fp16_weights=True).
+ */
+lli8_status_t lli8_quant_weight_rowwise(const void* W, int64_t N, int64_t K,
+                                        lli8_dtype_t dtype, int8_t* CB,
+                                        float* SCB, void* stream);
+
+/*
+ * Activation split and quantisation, "Core idea of LLM.int8()" steps 1-2;
+ * record "LLM.int8() / bitsandbytes int8", field "Activation scheme" (the
+ * outlier unit is the feature column, found at run time per matmul).
+ *   X      [T, K] fp16/bf16 (read)
+ *   CA     [T, K] int8 (written): codes of X with outlier columns set to 0
+ *   SCA    [T] fp32 (written): max over non-outlier k of |X[t, k]|
+ *   bitmap [ceil(K/32)] uint32 (written): bit (c % 32) of word c / 32 is set
+ *          when column c is an outlier
+ *   idx    [K] int32 (written): the first *n_idx entries are the outlier
+ *          columns in ascending order (the module's state.idx); the rest are
+ *          left as they were
+ *   n_idx  [1] int32 (written, device): number of outlier columns
+ */
+lli8_status_t lli8_quant_rowwise_outliers(const void* X, int64_t T, int64_t K,
+                                          lli8_dtype_t dtype, float threshold,
+                                          int8_t* CA, float* SCA,
+                                          uint32_t* bitmap, int32_t* idx,
+                                          int32_t* n_idx, void* stream);
+
+/*
+ * Buffers of one forward call.  The caller owns all of them.  After the call
+ * CA, SCA, bitmap, idx and n_idx hold this call's values exactly as
+ * lli8_quant_rowwise_outliers defines them.  acc, when not NULL, receives the
+ * int32 products acc[t, n] = sum_k CA[t, k] * CB[n, k] ([T, N] row-major).
+ * scratch is internal storage of at least lli8_scratch_bytes(T, K, dtype)
+ * bytes (the gathered outlier columns of X).
+ */
+typedef struct lli8_workspace {
+  int8_t* CA;
+  float* SCA;
+  uint32_t* bitmap;
+  int32_t* idx;
+  int32_t* n_idx;
+  int32_t* acc;     /* optional */
+  void* scratch;
+  size_t scratch_bytes;
+} lli8_workspace_t;
+
+/* Bytes of scratch lli8_int8_linear needs for these sizes. */
+size_t lli8_scratch_bytes(int64_t T, int64_t K, lli8_dtype_t dtype);
+
+/*
+ * The whole forward, "Core idea of LLM.int8()" steps 1-3:
+ *   out[t, n] = acc[t, n] * SCA[t] * SCB[n] / 127^2
+ *             + sum over outlier columns c of X[t, c] * What[n, c]
+ *             + bias[n]
+ * with What[n, c] = dtype(fl32(fl32(CB[n, c] * SCB[n]) / 127)), the recovery
+ * form of "Integration into transformers", accumulated in fp32 and rounded
+ * once to the output dtype.
+ *   X    [T, K] fp16/bf16 (read)      CB [N, K] int8, SCB [N] fp32 (read)
+ *   bias [N] fp16/bf16 or NULL        out [T, N] fp16/bf16 (written)
+ * The outlier set is taken from this call's X.
+ */
+lli8_status_t lli8_int8_linear(const void* X, int64_t T, int64_t K, int64_t N,
+                               lli8_dtype_t dtype, const int8_t* CB,
+                               const float* SCB, const void* bias,
+                               float threshold, void* out,
+                               const lli8_workspace_t* ws, void* stream);
+
+/*
+ * Optional kernel timing, for profiling.  While enabled (process-wide), each
+ * kernel the entry points enqueue is bracketed by two HIP events recorded on
+ * the call's stream.  lli8_trace_read waits for those events and reports the
+ * kernels enqueued since the previous read (at most LLI8_TRACE_MAX; later
+ * ones are not recorded), one entry each with its name and elapsed
+ * milliseconds, then starts a new record.  Not for concurrent use from
+ * several threads.  Disabled by default; the events are created on first use
+ * and kept until the process ends.
+ */
+#define LLI8_TRACE_MAX 8
+typedef struct lli8_trace {
+  int n;                             /* kernels since the last read */
+  const char* name[LLI8_TRACE_MAX];  /* static strings           */
+  float ms[LLI8_TRACE_MAX];
+} lli8_trace_t;
+
+void lli8_trace_enable(int on);
+lli8_status_t lli8_trace_read(lli8_trace_t* out);
+
+/* Static text for a status code. */
+const char* lli8_status_string(lli8_status_t s);
+
+/* Detail of the last LLI8_ERR_HIP or validation error on this thread. */
+const char* lli8_last_error(void);
+
+/* Library version, "major.minor.patch". */
+const char* lli8_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* LLI8_H */

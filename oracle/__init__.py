@@ -6,7 +6,7 @@ library.  Parity unpinned: the exact output bits (tolerance only).
 """
 from .lli8_oracle import *  # noqa: F401,F403
 from .lli8_oracle import (absmax_quantize_rows, decode_bits, dequantize,  # noqa: F401
-                          int8_accumulate, linear_forward, outlier_columns,
+                          int8_accumulate, linear_forward, outlier_bitmap, outlier_columns,
                           quantize_activations, quantize_weight,
                           quantize_weight_bits, recover_weight,
                           round_half_away, round_to_dtype_bits)

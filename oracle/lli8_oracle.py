@@ -116,6 +116,18 @@ def outlier_columns(X: np.ndarray, threshold: float) -> np.ndarray:
     return np.nonzero(col_max > tau)[0].astype(np.int32)
 
 
+def outlier_bitmap(idx: np.ndarray, K: int) -> np.ndarray:
+    """The outlier set as uint32 words: bit (c % 32) of word c // 32 is set for c in idx.
+
+    (An encoding of O2's set for the library's interface; the pages only name
+    the set, state.idx.)
+    """
+    words = np.zeros((K + 31) // 32, dtype=np.uint64)
+    idx = np.asarray(idx, dtype=np.int64)
+    np.bitwise_or.at(words, idx // 32, np.uint64(1) << (idx % 32).astype(np.uint64))
+    return words.astype(np.uint32)
+
+
 # ---------------------------------------------- O3-O6: absmax quantisation ----
 
 def round_half_away(v: np.ndarray) -> np.ndarray:

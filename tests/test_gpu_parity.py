@@ -1,0 +1,184 @@
+"""Parity of the HIP path (through the C-ABI) with the CPU oracle.
+
+Bit-exact: CB, SCB, CA, SCA, the outlier bitmap, idx, n_idx and the int32
+accumulators.  Output: normwise max-abs-rel <= 1e-2 (fp32 accumulation order
+and the single final rounding differ from the oracle's float64 sum).
+"""
+import numpy as np
+import pytest
+
+import oracle as O
+from tests.gpu_helpers import OUT_TOL, bits_of, normwise_rel, to_dev
+from workloads import config_case, make_case, random_case
+
+pytestmark = pytest.mark.gpu
+
+
+def _lib():
+    import bit_quantized_matmul_amd as B
+    return B
+
+
+def _run(case, threshold=None, want_acc=True):
+    """Quantise W on the GPU (placement step), run the forward; return everything."""
+    B = _lib()
+    import torch
+    tau = case.threshold if threshold is None else threshold
+    X = to_dev(case.X, case.dtype)
+    W = to_dev(case.W, case.dtype)
+    bias = to_dev(case.bias, case.dtype) if case.bias is not None else None
+    CB, SCB = B.lli8_quant_weight_rowwise(W)
+    out, ws = B.lli8_int8_linear(X, CB, SCB, bias, tau, want_acc=want_acc)
+    torch.cuda.synchronize()
+    n = int(ws.n_idx.item())
+    return dict(CB=CB.cpu().numpy(), SCB=SCB.cpu().numpy(), CA=ws.CA.cpu().numpy(),
+                SCA=ws.SCA[:case.T].cpu().numpy(), bitmap=ws.bitmap.cpu().numpy().view(np.uint32),
+                idx=ws.idx[:n].cpu().numpy(), n=n,
+                acc=ws.acc.cpu().numpy() if want_acc else None, out=bits_of(out))
+
+
+def _check_full(case, threshold=None):
+    tau = case.threshold if threshold is None else threshold
+    g = _run(case, tau)
+    CB, SCB = O.quantize_weight_bits(case.W, case.dtype)
+    assert np.array_equal(g["SCB"], SCB), "SCB"
+    assert np.array_equal(g["CB"], CB), "CB"
+    r = O.linear_forward(case.X, case.dtype, CB, SCB, case.bias, tau)
+    assert g["n"] == r["idx"].size, "n_idx"
+    assert np.array_equal(g["idx"], r["idx"]), "idx"
+    assert np.array_equal(g["bitmap"], O.outlier_bitmap(r["idx"], case.K)), "bitmap"
+    assert np.array_equal(g["SCA"], r["SCA"]), "SCA"
+    assert np.array_equal(g["CA"], r["CA"]), "CA"
+    assert np.array_equal(g["acc"], r["acc"]), "acc"
+    err = normwise_rel(g["out"], r["out64"], case.dtype)
+    assert err <= OUT_TOL, f"out normwise rel err {err}"
+    return g, r
+
+
+def test_tiny_config():
+    case = config_case("tiny")
+    g, r = _check_full(case)
+    assert g["idx"].tolist() == [3, 17]
+
+
+SHAPES = [
+    (1, 64, 64), (3, 24, 5), (8, 8, 4), (16, 4096, 130), (17, 520, 300), (33, 136, 65),
+    (100, 264, 257), (130, 1000, 129), (257, 512, 513), (300, 136, 40), (64, 8, 1), (5, 100, 7),
+    (2, 17, 3), (40, 37, 11), (600, 640, 520),
+]
+
+
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+@pytest.mark.parametrize("T,K,N", SHAPES)
+def test_random_shapes(T, K, N, dtype):
+    case = random_case(T, K, N, dtype=dtype, seed=T * 7 + K * 3 + N, n_out=min(3, K))
+    _check_full(case)
+
+
+@pytest.mark.parametrize("tau", [0.0, -1.0, float("inf"), 0.1, 2.5])
+def test_thresholds(tau):
+    case = random_case(40, 200, 70, seed=11, n_out=4)
+    g, r = _check_full(case, tau)
+    if tau <= 0 or tau == float("inf"):
+        assert g["n"] == 0
+    if tau == 0.1:
+        assert g["n"] == case.K  # every column flagged, as in the issue's repro
+
+
+def test_issue_repro_shape_all_columns():
+    """x[2, 8] with threshold 0.1 flags all 8 columns (state.idx = [0..7])."""
+    rng = np.random.default_rng(1609)
+    x = rng.standard_normal((2, 8)).astype(np.float32)
+    case = make_case("issue", 2, 8, 4, n_out=0, bias="normal", threshold=0.1, seed=1609)
+    case.X = x.astype(np.float16).view(np.uint16)
+    g, r = _check_full(case)
+    assert g["idx"].tolist() == list(range(8))
+    assert not g["CA"].any() and not g["SCA"].any() and not g["acc"].any()
+
+
+def test_threshold_edge_exact_value():
+    """A column whose largest magnitude is exactly the threshold is not flagged."""
+    case = random_case(12, 64, 16, seed=4, n_out=0)
+    x = O.decode_bits(case.X, "f16").copy()
+    x[:, 5] = 0.5
+    x[3, 5] = 6.0
+    x[:, 9] = 0.25
+    x[7, 9] = -6.00390625
+    case.X = x.astype(np.float16).view(np.uint16)
+    g, r = _check_full(case, 6.0)
+    assert g["idx"].tolist() == [9]
+
+
+def test_zero_rows_and_columns():
+    case = random_case(20, 96, 33, seed=8, n_out=2)
+    x = O.decode_bits(case.X, "f16").copy()
+    x[4] = 0.0          # a zero row: SCA = 0, CA = 0
+    x[:, 50] = 0.0      # a zero column
+    case.X = x.astype(np.float16).view(np.uint16)
+    w = O.decode_bits(case.W, "f16").copy()
+    w[3] = 0.0          # a zero weight row: SCB = 0
+    case.W = w.astype(np.float16).view(np.uint16)
+    g, r = _check_full(case)
+    assert g["SCA"][4] == 0 and not g["CA"][4].any()
+    assert g["SCB"][3] == 0
+
+
+def test_empty_T():
+    B = _lib()
+    import torch
+    X = torch.zeros((0, 64), dtype=torch.float16, device="cuda")
+    W = torch.randn((32, 64), dtype=torch.float16, device="cuda")
+    CB, SCB = B.lli8_quant_weight_rowwise(W)
+    out, ws = B.lli8_int8_linear(X, CB, SCB, None, 6.0)
+    torch.cuda.synchronize()
+    assert out.shape == (0, 32)
+    assert int(ws.n_idx.item()) == 0
+    assert not ws.bitmap.any()
+
+
+def test_activation_split_entry_point():
+    """lli8_quant_rowwise_outliers alone gives the same CA/SCA/idx as the oracle."""
+    B = _lib()
+    case = random_case(50, 320, 8, seed=21, n_out=5)
+    CA, SCA, bitmap, idx, n_idx = B.lli8_quant_rowwise_outliers(to_dev(case.X, "f16"), 6.0)
+    X = O.decode_bits(case.X, "f16")
+    ridx, rCA, rSCA = O.quantize_activations(X, 6.0)
+    n = int(n_idx.item())
+    assert np.array_equal(idx[:n].cpu().numpy(), ridx)
+    assert np.array_equal(CA.cpu().numpy(), rCA)
+    assert np.array_equal(SCA.cpu().numpy(), rSCA)
+    assert np.array_equal(bitmap.cpu().numpy().view(np.uint32), O.outlier_bitmap(ridx, case.K))
+
+
+def test_rounding_halves_on_gpu():
+    """Row [127, 2.5, -2.5, 0.5, 1.5, -0.5] codes to [127, 3, -3, 1, 2, -1]."""
+    B = _lib()
+    import torch
+    x = torch.tensor([[127, 2.5, -2.5, 0.5, 1.5, -0.5, 0, 0]], dtype=torch.float16, device="cuda")
+    CA, SCA, _, _, n = B.lli8_quant_rowwise_outliers(x, 0.0)
+    assert CA.cpu().tolist()[0][:6] == [127, 3, -3, 1, 2, -1]
+    CB, SCB = B.lli8_quant_weight_rowwise(x)
+    assert CB.cpu().tolist()[0][:6] == [127, 3, -3, 1, 2, -1]
+
+
+def test_deterministic_repeat():
+    case = random_case(300, 512, 260, seed=3, n_out=6)
+    a = _run(case)
+    b = _run(case)
+    for k in ("CA", "SCA", "idx", "acc", "out"):
+        assert np.array_equal(a[k], b[k]), k
+
+
+def test_leading_dims_flatten():
+    """nn.Linear semantics: leading dims flatten into T."""
+    B = _lib()
+    import torch
+    case = random_case(2 * 3 * 5, 64, 24, seed=9, n_out=2)
+    X = to_dev(case.X, "f16")
+    W = to_dev(case.W, "f16")
+    CB, SCB = B.lli8_quant_weight_rowwise(W)
+    out2, _ = B.lli8_int8_linear(X, CB, SCB, None, 6.0)
+    out3, _ = B.lli8_int8_linear(X.view(2, 3, 5, 64), CB, SCB, None, 6.0)
+    torch.cuda.synchronize()
+    assert out3.shape == (2, 3, 5, 24)
+    assert torch.equal(out3.reshape(30, 24), out2)

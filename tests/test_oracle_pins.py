@@ -334,3 +334,14 @@ def test_fp16_rounding_from_float64_is_single_rounding():
     vb = np.array([1 + 2.0 ** -8 + 2.0 ** -40, 1 + 2.0 ** -8], np.float64)
     bb = O.decode_bits(O.round_to_dtype_bits(vb, "bf16"), "bf16")
     assert bb.tolist() == [1 + 2.0 ** -7, 1.0]
+
+
+def test_outlier_bitmap_encoding():
+    """Bit c % 32 of word c // 32 marks column c; brute-force decode gives idx back."""
+    K = 100
+    idx = np.array([0, 3, 31, 32, 63, 64, 99], np.int32)
+    words = O.outlier_bitmap(idx, K)
+    assert words.dtype == np.uint32 and words.size == 4
+    back = [c for c in range(K) if (int(words[c // 32]) >> (c % 32)) & 1]
+    assert back == idx.tolist()
+    assert words[0] == (1 | (1 << 3) | (1 << 31))
