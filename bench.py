@@ -5,15 +5,22 @@
 One step is one forward of the whole path over one synthetic batch: outlier
 column scan, row-wise activation quantisation, int8 GEMM with the fused
 dequantisation, 16-bit outlier product and bias (and, for the workloads whose
-weights are quantised on every call, the weight quantisation before it).  The
-inputs are resident in HBM before the timed region; before every step a
-1 GiB buffer is overwritten so that the 256 MB Infinity Cache and the L2s hold
-nothing of the step's operands (the flush is outside the step's events).
+weights are quantised on every call, the weight quantisation before it).
+
+Timing protocol.  All inputs are resident in HBM before the timed region.
+They exist in R identical copies at different addresses (R chosen so that one
+pass over the copies moves >= 768 MiB, three times the 256 MB Infinity
+Cache), and step i uses copy i mod R -- the way consecutive layers of a model
+stream different weights -- so no step finds its operands in cache.  The K
+steps run back to back between one pair of HIP events on the library's
+stream; ms_per_step is the elapsed time divided by K.  (A per-step event pair
+would add the ~6 us floor of an event-bracketed launch on this platform.)
 
 Prints one JSON line on stdout.  `value` is the effective throughput
-2*T*N*K / t in TOPS; `roofline` describes the kernel with the largest average
-duration, timed with HIP events on the library's stream inside the timed
-region; `cpu_baseline` times the CPU oracle on the host.
+2*T*N*K / t in TOPS.  `roofline` describes the kernel with the largest average
+duration: for a one-kernel step that is the step time above; otherwise a
+second pass of K steps records HIP events around each kernel on the library's
+stream.  `cpu_baseline` times the CPU oracle on the host.
 """
 from __future__ import annotations
 
@@ -39,7 +46,8 @@ def parse():
     p.add_argument("--steps", type=int, default=50)
     p.add_argument("--warmup", type=int, default=10)
     p.add_argument("--workload", default="decode")
-    p.add_argument("--no-flush", action="store_true", help="keep caches warm between steps")
+    p.add_argument("--rotate-mib", type=float, default=768.0,
+                   help="input copies are rotated until one pass moves this many MiB")
     p.add_argument("--cpu-seconds", type=float, default=10.0, help="target CPU-oracle time")
     p.add_argument("--no-cpu-baseline", action="store_true")
     return p.parse_args()
@@ -58,6 +66,8 @@ def kernel_bytes(name, case, n_idx):
         return 2 * T * K
     if name == "quant_weight":
         return 2 * N * K + N * K + 4 * N
+    if name == "decode_fused":  # the whole forward in one launch
+        return 2 * T * K + N * K + 4 * N + bias + 2 * T * N
     if name == "bitmap_clear":
         return 4 * ((K + 31) // 32)
     return 0
@@ -124,53 +134,70 @@ def main():
         t = torch.from_numpy(np.ascontiguousarray(bits).view(np.int16))
         return t.view(torch.float16 if case.dtype == "f16" else torch.bfloat16).to(dev)
 
-    X = to_dev(case.X)
-    W = to_dev(case.W)
-    bias = to_dev(case.bias) if case.bias is not None else None
+    X0 = to_dev(case.X)
+    W0 = to_dev(case.W)
+    bias0 = to_dev(case.bias) if case.bias is not None else None
     T, K, N = case.T, case.K, case.N
-    CB = torch.empty((N, K), dtype=torch.int8, device=dev)
-    SCB = torch.empty((N,), dtype=torch.float32, device=dev)
-    B.lli8_quant_weight_rowwise(W, CB, SCB)          # placement (untimed unless quantised per call)
-    ws = B.Workspace(T, K, N, X.dtype, dev)
-    out = torch.empty((T, N), dtype=X.dtype, device=dev)
-    flush = None if args.no_flush else torch.empty(1 << 30, dtype=torch.uint8, device=dev)
-
-    def step():
+    CB0 = torch.empty((N, K), dtype=torch.int8, device=dev)
+    SCB0 = torch.empty((N,), dtype=torch.float32, device=dev)
+    B.lli8_quant_weight_rowwise(W0, CB0, SCB0)   # placement (untimed unless quantised per call)
+    copy_bytes = X0.numel() * 2 + (W0.numel() * 2 if case.weights_each_call else CB0.numel() + SCB0.numel() * 4) \
+        + (bias0.numel() * 2 if bias0 is not None else 0)
+    R = max(1, min(64, -(-int(args.rotate_mib * 2 ** 20) // copy_bytes)))
+    copies = []
+    for r in range(R):
+        cp = dict(X=X0 if r == 0 else X0.clone(), bias=None if bias0 is None else (bias0 if r == 0 else bias0.clone()))
         if case.weights_each_call:
-            B.lli8_quant_weight_rowwise(W, CB, SCB)
-        B.lli8_int8_linear(X, CB, SCB, bias, case.threshold, out=out, ws=ws)
+            cp["W"] = W0 if r == 0 else W0.clone()
+            cp["CB"] = CB0 if r == 0 else torch.empty_like(CB0)
+            cp["SCB"] = SCB0 if r == 0 else torch.empty_like(SCB0)
+        else:
+            cp["CB"] = CB0 if r == 0 else CB0.clone()
+            cp["SCB"] = SCB0 if r == 0 else SCB0.clone()
+        copies.append(cp)
+    if not case.weights_each_call:
+        del W0
+    ws = B.Workspace(T, K, N, X0.dtype, dev)
+    out = torch.empty((T, N), dtype=X0.dtype, device=dev)
+
+    def step(i):
+        cp = copies[i % R]
+        if case.weights_each_call:
+            B.lli8_quant_weight_rowwise(cp["W"], cp["CB"], cp["SCB"])
+        B.lli8_int8_linear(cp["X"], cp["CB"], cp["SCB"], cp["bias"], case.threshold, out=out, ws=ws)
 
     for i in range(args.warmup):
-        if flush is not None:
-            flush.fill_(i & 0xFF)
-        step()
+        step(i)
     torch.cuda.synchronize()
     n_idx = int(ws.n_idx.item())
 
-    B.lli8_trace_enable(True)
-    B.lli8_trace_read()  # start a fresh record
-    kern_ms = {}
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-          for _ in range(args.steps)]
+    # timed region: K steps back to back
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     t_wall = time.perf_counter()
+    e0.record()
     for i in range(args.steps):
-        if flush is not None:
-            flush.fill_((i + 7) & 0xFF)
-        ev[i][0].record()
-        step()
-        ev[i][1].record()
-        for name, ms in B.lli8_trace_read():
-            kern_ms.setdefault(name, []).append(ms)
+        step(args.warmup + i)
+    e1.record()
     torch.cuda.synchronize()
     t_wall = time.perf_counter() - t_wall
-    B.lli8_trace_enable(False)
-    step_ms = [a.elapsed_time(b) for a, b in ev]
-    ms = sum(step_ms) / len(step_ms)
+    ms = e0.elapsed_time(e1) / args.steps
 
+    # per-kernel durations: a second pass with events around each kernel
+    B.lli8_trace_enable(True)
+    B.lli8_trace_read()
+    kern_ms = {}
+    for i in range(args.steps):
+        step(i)
+        for name, kms in B.lli8_trace_read():
+            kern_ms.setdefault(name, []).append(kms)
+    torch.cuda.synchronize()
+    B.lli8_trace_enable(False)
+    avg = {k: sum(v) / len(v) for k, v in kern_ms.items()}
+    if len(avg) == 1:
+        avg = {k: ms for k in avg}  # one kernel per step: the timed region is that kernel
     ops = 2.0 * T * N * K
     value = ops / (ms * 1e-3) / 1e12
-    avg = {k: sum(v) / len(v) for k, v in kern_ms.items()}
     dom = max(avg, key=avg.get)
     dom_ms = avg[dom]
     if dom == "int8_gemm" and ops / kernel_bytes(dom, case, n_idx) > INT8_PEAK_TOPS / HBM_PEAK_GBS * 1e3:
@@ -196,7 +223,7 @@ def main():
         "config": {"workload": args.workload, "T": T, "K": K, "N": N, "act_dtype": case.dtype,
                    "threshold": case.threshold, "n_idx": n_idx, "bias": case.bias is not None,
                    "weights": "quantised every call" if case.weights_each_call else "pre-quantised",
-                   "cache_flush_between_steps": flush is not None,
+                   "input_copies_rotated": R, "rotation_mib": round(R * copy_bytes / 2 ** 20, 1),
                    "step_algorithmic_bytes": step_bytes(case),
                    "step_hbm_frac": round(step_bytes(case) / (ms * 1e-3) / (HBM_PEAK_GBS * 1e9), 4),
                    "kernels_ms": {k: round(v, 5) for k, v in avg.items()},

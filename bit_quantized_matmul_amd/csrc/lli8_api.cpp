@@ -4,6 +4,7 @@
 #include <math.h>
 #include <stdarg.h>
 #include <stdio.h>
+#include <stdlib.h>
 #include <string.h>
 
 #include <hip/hip_runtime.h>
@@ -100,6 +101,13 @@ lli8_status_t trace_end(hipStream_t s) {
     TRY(hip_status((launch), name));                                           \
     TRY(trace_end(stream));                                                    \
   } while (0)
+
+// The single-launch decode path can be switched off (LLI8_FUSED_DECODE=0) to
+// run the general kernels for small T as well.
+bool fused_decode_enabled() {
+  const char* v = getenv("LLI8_FUSED_DECODE");
+  return !(v != nullptr && v[0] == '0');
+}
 
 // Outliers are looked for only for a finite positive threshold.
 bool outliers_enabled(float tau) { return tau > 0.0f && isfinite(tau); }
@@ -221,6 +229,27 @@ lli8_status_t lli8_int8_linear(const void* X, int64_t T, int64_t K, int64_t N, l
     if (!aligned16(ws->scratch)) return fail(LLI8_ERR_ALIGN, "ws->scratch is not 16-byte aligned");
   }
   hipStream_t s = static_cast<hipStream_t>(stream);
+  if (T > 0 && lli8::decode_fused_supported(T, K) && fused_decode_enabled()) {
+    lli8::FusedArgs f;
+    f.dt = (int)dtype;
+    f.X = X;
+    f.T = T;
+    f.K = K;
+    f.N = N;
+    f.tau = outl ? threshold : 0.0f;
+    f.CB = CB;
+    f.SCB = SCB;
+    f.bias = bias;
+    f.out = out;
+    f.CA = ws->CA;
+    f.SCA = ws->SCA;
+    f.bitmap = ws->bitmap;
+    f.idx = ws->idx;
+    f.n_idx = ws->n_idx;
+    f.acc = ws->acc;
+    TRACED(s, "decode_fused", lli8::launch_decode_fused(f, s));
+    return LLI8_OK;
+  }
   TRY(enqueue_activation_split(X, T, K, (int)dtype, threshold, ws->CA, ws->SCA, ws->bitmap, ws->idx, ws->n_idx,
                                outl ? ws->scratch : nullptr, s));
   lli8::LinearArgs a;

@@ -35,4 +35,25 @@ struct LinearArgs {
 
 hipError_t launch_linear_gemm(const LinearArgs& a, hipStream_t s);
 
+// Fused single-launch path for T <= 16 (outlier scan, quantisation, GEMM).
+struct FusedArgs {
+  int dt;
+  const void* X;
+  int64_t T, K, N;
+  float tau;
+  const int8_t* CB;
+  const float* SCB;
+  const void* bias;  // may be null
+  void* out;
+  int8_t* CA;
+  float* SCA;
+  uint32_t* bitmap;
+  int32_t* idx;
+  int32_t* n_idx;
+  int32_t* acc;      // may be null
+};
+
+bool decode_fused_supported(int64_t T, int64_t K);
+hipError_t launch_decode_fused(const FusedArgs& a, hipStream_t s);
+
 }  // namespace lli8

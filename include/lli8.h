@@ -105,7 +105,9 @@ lli8_status_t lli8_quant_rowwise_outliers(const void* X, int64_t T, int64_t K,
  * lli8_quant_rowwise_outliers defines them.  acc, when not NULL, receives the
  * int32 products acc[t, n] = sum_k CA[t, k] * CB[n, k] ([T, N] row-major).
  * scratch is internal storage of at least lli8_scratch_bytes(T, K, dtype)
- * bytes (the gathered outlier columns of X).
+ * bytes (the gathered outlier columns of X), required when the threshold
+ * enables outlier columns.  Calls sharing one workspace must be ordered on
+ * one stream.
  */
 typedef struct lli8_workspace {
   int8_t* CA;

@@ -182,3 +182,31 @@ def test_leading_dims_flatten():
     torch.cuda.synchronize()
     assert out3.shape == (2, 3, 5, 24)
     assert torch.equal(out3.reshape(30, 24), out2)
+
+
+SMALL_T = [(1, 64, 64), (3, 48, 5), (16, 4096, 130), (8, 8192, 40), (16, 8448, 33), (5, 1024, 4097),
+           (16, 256, 16), (2, 512, 3000), (11, 2048, 1000), (16, 64, 8192)]
+
+
+@pytest.mark.parametrize("fused", ["1", "0"])
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+@pytest.mark.parametrize("T,K,N", SMALL_T)
+def test_small_T_both_decode_paths(T, K, N, dtype, fused, monkeypatch):
+    """T <= 16 runs the single-launch path by default; LLI8_FUSED_DECODE=0 selects the
+    multi-kernel path.  Both must match the oracle."""
+    monkeypatch.setenv("LLI8_FUSED_DECODE", fused)
+    case = random_case(T, K, N, dtype=dtype, seed=T + K + N, n_out=min(4, K))
+    _check_full(case)
+
+
+@pytest.mark.parametrize("tau", [0.0, 0.1, 2.0, float("inf")])
+def test_fused_decode_thresholds(tau):
+    """Degenerate and dense thresholds on the single-launch path (T <= 16)."""
+    case = random_case(16, 1024, 512, seed=77, n_out=3)
+    _check_full(case, tau)
+
+
+def test_fused_decode_many_blocks_per_workgroup():
+    """N well beyond one 16-feature block per CU: each workgroup walks several blocks."""
+    case = random_case(7, 512, 16 * 256 * 3 + 5, seed=78, n_out=2)
+    _check_full(case)
