@@ -23,35 +23,17 @@
 
 namespace lli8 {
 
-constexpr int BK = 64;  // bytes of K staged per step (= int8 elements)
-
-// LDS address of 16-byte chunk c (0..3) of row r in a 64-byte-row tile.  The
-// XOR spreads the eight rows that one ds_read_b128 phase touches over all 32
-// banks, for both the row-wise writes and the MFMA-operand reads.
-__device__ __forceinline__ int lds_off(int r, int c) { return r * 64 + ((c ^ ((r >> 1) & 3)) << 4); }
-
-__device__ __forceinline__ u32x4 load16_i8(const int8_t* __restrict__ base, int64_t row, int64_t nrows,
-                                           int64_t K, int64_t k, bool vec) {
-  u32x4 z = {0u, 0u, 0u, 0u};
-  if (row >= nrows) return z;
-  const int8_t* p = base + row * K;
-  if (vec) {
-    if (k < K) z = *reinterpret_cast<const u32x4*>(p + k);
-    return z;
-  }
-  uint32_t w[4] = {0u, 0u, 0u, 0u};
-#pragma unroll
-  for (int b = 0; b < 16; ++b) {
-    const int64_t kk = k + b;
-    const uint32_t v = (kk < K) ? (uint32_t)(uint8_t)p[kk] : 0u;
-    w[b >> 2] |= v << (8 * (b & 3));
-  }
-  z[0] = w[0];
-  z[1] = w[1];
-  z[2] = w[2];
-  z[3] = w[3];
-  return z;
+// LDS address of 16-byte chunk c of row r in a tile with KB-byte rows.  A
+// 16-byte-per-lane LDS access is served 16 lanes (256 bytes, all 64 banks) at
+// a time; the XOR gives the 16 consecutive rows that an MFMA-operand read
+// touches (same logical chunk) 16 distinct 16-byte bank groups, and keeps the
+// row-wise tile writes conflict-free too.
+template <int KB>
+__device__ __forceinline__ int tile_off(int r, int c) {
+  if constexpr (KB == 64) return r * 64 + ((c ^ ((r >> 2) & 3)) << 4);
+  else return r * 128 + ((c ^ ((r >> 1) & 7)) << 4);
 }
+__device__ __forceinline__ int lds_off(int r, int c) { return tile_off<64>(r, c); }
 
 // Recovered weight value for the 16-bit product: dtype(fl32(fl32(cb*scb)/127)).
 template <int DT>
@@ -87,7 +69,7 @@ __device__ __forceinline__ void tile_coords(int b, int tiles_m, int tiles_n, int
   tn = in / gsz;
 }
 
-template <int DT, int BM, int BN, bool VEC>
+template <int DT, int BM, int BN, int KM, int BK>
 __global__ __launch_bounds__(256, 1) void linear_tile_kernel(
     const int8_t* __restrict__ CA, const int8_t* __restrict__ CB, const float* __restrict__ SCA,
     const float* __restrict__ SCB, const uint16_t* __restrict__ bias, const uint16_t* __restrict__ xo,
@@ -95,7 +77,9 @@ __global__ __launch_bounds__(256, 1) void linear_tile_kernel(
     int32_t* __restrict__ acc_out, int T, int N, int K, int tiles_m, int tiles_n) {
   constexpr int WM = BM / 2, WN = BN / 2;
   constexpr int FM = WM / 32, FN = WN / 32;
-  constexpr int LA = BM * 4 / 256, LB = BN * 4 / 256;  // 16-byte chunks per thread per step
+  constexpr int CPR = BK / 16;                          // 16-byte chunks per tile row
+  constexpr int SS = BK / 32;                           // MFMA sub-steps per K step
+  constexpr int LA = BM * CPR / 256, LB = BN * CPR / 256;  // 16-byte chunks per thread per step
   __shared__ __attribute__((aligned(16))) int8_t sA[2][BM * BK];
   __shared__ __attribute__((aligned(16))) int8_t sB[2][BN * BK];
 
@@ -112,58 +96,145 @@ __global__ __launch_bounds__(256, 1) void linear_tile_kernel(
 #pragma unroll
     for (int j = 0; j < FN; ++j) acc[i][j] = (v16i){0};
 
-  u32x4 ra[LA], rb[LB];
-  auto gload = [&](int kt) {
-    const int64_t k0 = (int64_t)kt * BK;
+  // Global loads run two K steps ahead in two register sets; LDS is double
+  // buffered.  Step kt: issue the loads of step kt + 2, multiply out of LDS
+  // buffer kt & 1, then store step kt + 1 (loaded one step earlier) into the
+  // other buffer.  Loads are branch-free so the compiler's wait counts stay
+  // exact: rows past T (N) are clamped to the last row and only feed
+  // accumulators that are never stored; steps past the end re-read the last
+  // one and are never stored; with K % 64 != 0 (KM >= 1) chunks past K are
+  // read at column 0 and zeroed before they reach LDS.
+  const int nk = (K + BK - 1) / BK;
+  const int8_t* pa[LA];
+  const int8_t* pb[LB];
 #pragma unroll
-    for (int i = 0; i < LA; ++i) {
-      const int q = tid + 256 * i, r = q >> 2, c = q & 3;
-      ra[i] = load16_i8(CA, m0 + r, T, K, k0 + c * 16, VEC);
-    }
+  for (int i = 0; i < LA; ++i) {
+    const int r = (tid + 256 * i) / CPR;
+    const int64_t row = m0 + r < T ? m0 + r : (int64_t)T - 1;
+    pa[i] = CA + row * K;
+  }
 #pragma unroll
-    for (int i = 0; i < LB; ++i) {
-      const int q = tid + 256 * i, r = q >> 2, c = q & 3;
-      rb[i] = load16_i8(CB, n0 + r, N, K, k0 + c * 16, VEC);
+  for (int i = 0; i < LB; ++i) {
+    const int r = (tid + 256 * i) / CPR;
+    const int64_t row = n0 + r < N ? n0 + r : (int64_t)N - 1;
+    pb[i] = CB + row * K;
+  }
+  const int cq = (tid % CPR) * 16;  // byte offset of this thread's chunk within a step
+  u32x4 ra0[LA], rb0[LB], ra1[LA], rb1[LB];
+  auto ld = [&](const int8_t* row, int k) -> u32x4 {
+    if constexpr (KM == 2) {  // K % 16 != 0: byte-wise, zero past K
+      uint32_t wv[4] = {0u, 0u, 0u, 0u};
+#pragma unroll
+      for (int bb = 0; bb < 16; ++bb) {
+        const int kk = k + bb;
+        const uint32_t v = (kk < K) ? (uint32_t)(uint8_t)row[kk] : 0u;
+        wv[bb >> 2] |= v << (8 * (bb & 3));
+      }
+      return (u32x4){wv[0], wv[1], wv[2], wv[3]};
+    } else {
+      return *reinterpret_cast<const u32x4*>(row + ((KM == 0 || k < K) ? k : 0));
     }
   };
-  auto lstore = [&](int buf) {
+  auto gload = [&](int kt, u32x4 (&ra)[LA], u32x4 (&rb)[LB]) {
+    const int k = min(kt, nk - 1) * BK + cq;
+#pragma unroll
+    for (int i = 0; i < LA; ++i) ra[i] = ld(pa[i], k);
+#pragma unroll
+    for (int i = 0; i < LB; ++i) rb[i] = ld(pb[i], k);
+  };
+  auto fix_tail = [&](int kt, u32x4 (&ra)[LA], u32x4 (&rb)[LB]) {
+    if constexpr (KM == 1) {
+      if (kt * BK + cq >= K) {
+#pragma unroll
+        for (int i = 0; i < LA; ++i) ra[i] = (u32x4){0u, 0u, 0u, 0u};
+#pragma unroll
+        for (int i = 0; i < LB; ++i) rb[i] = (u32x4){0u, 0u, 0u, 0u};
+      }
+    }
+  };
+  auto lstore = [&](int buf, const u32x4 (&ra)[LA], const u32x4 (&rb)[LB]) {
 #pragma unroll
     for (int i = 0; i < LA; ++i) {
-      const int q = tid + 256 * i, r = q >> 2, c = q & 3;
-      *reinterpret_cast<u32x4*>(&sA[buf][lds_off(r, c)]) = ra[i];
+      const int q = tid + 256 * i, r = q / CPR, c = q % CPR;
+      *reinterpret_cast<u32x4*>(&sA[buf][tile_off<BK>(r, c)]) = ra[i];
     }
 #pragma unroll
     for (int i = 0; i < LB; ++i) {
-      const int q = tid + 256 * i, r = q >> 2, c = q & 3;
-      *reinterpret_cast<u32x4*>(&sB[buf][lds_off(r, c)]) = rb[i];
+      const int q = tid + 256 * i, r = q / CPR, c = q % CPR;
+      *reinterpret_cast<u32x4*>(&sB[buf][tile_off<BK>(r, c)]) = rb[i];
+    }
+  };
+  // MFMA operands for one 32-deep sub-step s of a step.
+  auto read_frags = [&](int buf, int s, v4i (&fa)[FM], v4i (&fb)[FN]) {
+    const int c = 2 * s + (lane >> 5);
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+      fa[i] = *reinterpret_cast<const v4i*>(&sA[buf][tile_off<BK>(wm * WM + i * 32 + (lane & 31), c)]);
+#pragma unroll
+    for (int j = 0; j < FN; ++j)
+      fb[j] = *reinterpret_cast<const v4i*>(&sB[buf][tile_off<BK>(wn * WN + j * 32 + (lane & 31), c)]);
+  };
+  auto mfmas = [&](const v4i (&fa)[FM], const v4i (&fb)[FN]) {
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+      for (int j = 0; j < FN; ++j)
+        acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(fa[i], fb[j], acc[i][j], 0, 0, 0);
+  };
+  v4i fa0[FM], fb0[FN], fa1[FM], fb1[FN];
+  // One K step out of buffer `cur` (its sub-step 0 operands already in set 0):
+  // while sub-step s multiplies, the operands of sub-step s + 1 are read;
+  // before the last sub-step, the next step is stored into the other buffer,
+  // then one barrier, then the next step's sub-step 0 operands are read while
+  // the last sub-step multiplies.  Every MFMA block finds its operands
+  // loaded, and one barrier per step suffices (a buffer is rewritten only
+  // after the barrier that follows its last read).
+  auto step = [&](int cur, int kt, u32x4 (&la)[LA], u32x4 (&lb)[LB], u32x4 (&sa)[LA], u32x4 (&sb)[LB]) {
+    gload(kt + 2, la, lb);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int s = 0; s < SS; ++s) {
+      if (s + 1 < SS) {
+        if (s % 2 == 0) read_frags(cur, s + 1, fa1, fb1);
+        else read_frags(cur, s + 1, fa0, fb0);
+      } else {
+        fix_tail(kt + 1, sa, sb);
+        lstore(cur ^ 1, sa, sb);
+        __syncthreads();
+        read_frags(cur ^ 1, 0, fa0, fb0);  // SS is even: the last sub-step uses set 1
+      }
+      __builtin_amdgcn_sched_barrier(0);
+      if (s % 2 == 0) mfmas(fa0, fb0);
+      else mfmas(fa1, fb1);
+      __builtin_amdgcn_sched_barrier(0);
     }
   };
 
-  const int nk = (K + BK - 1) / BK;
-  gload(0);
-  lstore(0);
+  gload(0, ra0, rb0);
+  gload(1, ra1, rb1);
+  fix_tail(0, ra0, rb0);
+  lstore(0, ra0, rb0);
   __syncthreads();
-  for (int kt = 0; kt < nk; ++kt) {
-    const int cur = kt & 1;
-    if (kt + 1 < nk) gload(kt + 1);
+  read_frags(0, 0, fa0, fb0);
+  // Two steps per trip, no branch inside: on entry buffer 0 holds step kt
+  // (sub-step 0 operands in set 0) and register set 1 holds step kt + 1.
+  // Steps loaded or stored past the end are re-reads of the last one and are
+  // never multiplied.
+  int kt = 0;
+  for (; kt + 2 <= nk; kt += 2) {
+    step(0, kt, ra0, rb0, ra1, rb1);
+    step(1, kt + 1, ra1, rb1, ra0, rb0);
+  }
+  if (kt < nk) {  // odd step count: the last step sits in buffer 0
 #pragma unroll
-    for (int s = 0; s < 2; ++s) {
-      const int c = 2 * s + (lane >> 5);
-      v4i a[FM], b[FN];
-#pragma unroll
-      for (int i = 0; i < FM; ++i)
-        a[i] = *reinterpret_cast<const v4i*>(&sA[cur][lds_off(wm * WM + i * 32 + (lane & 31), c)]);
-#pragma unroll
-      for (int j = 0; j < FN; ++j)
-        b[j] = *reinterpret_cast<const v4i*>(&sB[cur][lds_off(wn * WN + j * 32 + (lane & 31), c)]);
-#pragma unroll
-      for (int i = 0; i < FM; ++i)
-#pragma unroll
-        for (int j = 0; j < FN; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(a[i], b[j], acc[i][j], 0, 0, 0);
+    for (int s = 0; s < SS; ++s) {
+      if (s + 1 < SS) {
+        if (s % 2 == 0) read_frags(0, s + 1, fa1, fb1);
+        else read_frags(0, s + 1, fa0, fb0);
+      }
+      if (s % 2 == 0) mfmas(fa0, fb0);
+      else mfmas(fa1, fb1);
     }
-    if (kt + 1 < nk) lstore(cur ^ 1);
-    __syncthreads();
   }
 
   // ---- epilogue.  32x32 accumulator layout: lane holds column (lane & 31),
@@ -339,12 +410,13 @@ __global__ __launch_bounds__(256) void linear_decode_kernel(
   }
 }
 
-template <int DT, int BM, int BN>
+template <int DT, int BM, int BN, int BK>
 static hipError_t launch_tile(const LinearArgs& a, hipStream_t s) {
   const int tiles_m = (int)((a.T + BM - 1) / BM), tiles_n = (int)((a.N + BN - 1) / BN);
   const int nb = tiles_m * tiles_n;
-  const bool vec = (a.K % 16) == 0;
-  auto k = vec ? linear_tile_kernel<DT, BM, BN, true> : linear_tile_kernel<DT, BM, BN, false>;
+  auto k = (a.K % BK) == 0 ? linear_tile_kernel<DT, BM, BN, 0, BK>
+           : (a.K % 16) == 0 ? linear_tile_kernel<DT, BM, BN, 1, BK>
+                             : linear_tile_kernel<DT, BM, BN, 2, BK>;
   k<<<dim3(nb), dim3(256), 0, s>>>(a.CA, a.CB, a.SCA, a.SCB, static_cast<const uint16_t*>(a.bias),
                                    static_cast<const uint16_t*>(a.xo), a.idx, a.n_idx,
                                    static_cast<uint16_t*>(a.out), a.acc, (int)a.T, (int)a.N, (int)a.K,
@@ -361,8 +433,8 @@ static hipError_t launch_linear_t(const LinearArgs& a, hipStream_t s) {
         a.idx, a.n_idx, static_cast<uint16_t*>(a.out), a.acc, (int)a.T, (int)a.N, (int)a.K);
     return hipGetLastError();
   }
-  if (a.T >= 512 && a.N >= 512) return launch_tile<DT, 256, 256>(a, s);
-  return launch_tile<DT, 128, 128>(a, s);
+  if (a.T >= 512 && a.N >= 512) return launch_tile<DT, 256, 256, 64>(a, s);
+  return launch_tile<DT, 128, 128, 64>(a, s);
 }
 
 hipError_t launch_linear_gemm(const LinearArgs& a, hipStream_t s) {
