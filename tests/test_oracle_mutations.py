@@ -100,3 +100,15 @@ def test_dropped_outlier_term_is_caught(monkeypatch):
     _reload_pins(monkeypatch, "linear_forward", no_outlier_forward)
     with pytest.raises(AssertionError):
         P.test_output_within_apriori_error_bound("bf16", 2)
+
+
+def test_dropped_bias_is_caught(monkeypatch):
+    """Drop the bias from the output sum: the a priori bound test fails."""
+    orig = M.linear_forward
+
+    def no_bias_forward(X_bits, dtype, CB, SCB, bias_bits, threshold, rows=None, cols=None):
+        return orig(X_bits, dtype, CB, SCB, None, threshold, rows, cols)
+
+    _reload_pins(monkeypatch, "linear_forward", no_bias_forward)
+    with pytest.raises(AssertionError):
+        P.test_output_within_apriori_error_bound("f16", 3)
