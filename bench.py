@@ -50,6 +50,9 @@ def parse():
                    help="input copies are rotated until one pass moves this many MiB")
     p.add_argument("--cpu-seconds", type=float, default=10.0, help="target CPU-oracle time")
     p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--copy-mib", type=float, default=0.0,
+                   help="instead of the benchmark, run 10 plain device-to-device copies of this "
+                        "many MiB (the calibration for HBM byte counters) and exit")
     return p.parse_args()
 
 
@@ -79,6 +82,43 @@ def step_bytes(case):
     bias = 2 * N if case.bias is not None else 0
     w = 2 * N * K if case.weights_each_call else N * K + 4 * N
     return 2 * T * K + w + bias + 2 * T * N
+
+
+KERNEL_SOURCES = {
+    "int8_gemm": "lli8_gemm.hip", "decode_fused": "lli8_decode.hip", "quant_activations": "lli8_quant.hip",
+    "outlier_scan": "lli8_quant.hip", "quant_weight": "lli8_quant.hip", "bitmap_clear": "lli8_quant.hip",
+}
+
+
+def measured_traffic(workload, kernel):
+    """HBM bytes per launch from the stored counter runs (FETCH_SIZE + WRITE_SIZE,
+    each scaled by what the counter reads for a plain copy of known size), or None
+    when none were taken for this kernel and workload or its source has changed since."""
+    import hashlib
+    path = os.path.join(ROOT, "profiles", "hbm_traffic.json")
+    src = KERNEL_SOURCES.get(kernel)
+    if src is None or not os.path.exists(path):
+        return None
+    with open(path) as f:
+        rec = json.load(f).get("kernels", {}).get(f"{workload}/{kernel}")
+    if rec is None:
+        return None
+    with open(os.path.join(ROOT, "bit_quantized_matmul_amd", "csrc", src), "rb") as f:
+        if hashlib.sha256(f.read()).hexdigest() != rec["source_sha256"]:
+            return None
+    return int(rec["bytes_per_launch"])
+
+
+def copy_calibration(mib):
+    """Ten device-to-device copies of `mib` MiB (one copy kernel each)."""
+    import torch
+    n = int(mib * 2 ** 20)
+    src = torch.ones(n, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(10):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_bytes_read": n, "copy_bytes_written": n, "copies": 10}), flush=True)
 
 
 def cpu_baseline(case, CB_np, SCB_np, seconds):
@@ -118,6 +158,9 @@ def main():
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
               "(this path is not sharded across GPUs).", file=sys.stderr)
         sys.exit(2)
+    if args.copy_mib > 0:
+        copy_calibration(args.copy_mib)
+        return
 
     import numpy as np
     import torch
@@ -211,7 +254,7 @@ def main():
         gbs = kernel_bytes(dom, case, n_idx) / (dom_ms * 1e-3) / 1e9
         roof = {"bound": "hbm", "achieved": round(gbs, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s"}
     roof["frac"] = round(roof["achieved"] / roof["peak"], 4)
-    roof["traffic"] = None
+    roof["traffic"] = measured_traffic(args.workload, dom)
     roof["kernel"] = dom
     roof["kernel_ms"] = round(dom_ms, 5)
 
