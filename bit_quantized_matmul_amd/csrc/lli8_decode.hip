@@ -1,47 +1,53 @@
 // Fused decode path (T <= 16, K <= 4096): the whole LLM.int8() forward in one
-// launch, with no workgroup ever waiting on another.  Eight waves per
-// workgroup (two per SIMD, so one wave's dependent arithmetic overlaps the
-// other's), each owning two 256-column slices of K.
+// launch, with no workgroup ever waiting on another.
 //
 // For a handful of tokens the int8 weight stream (N x K bytes) is the only
 // real HBM traffic; separate launches for the outlier scan, the activation
 // quantiser and the GEMM each cost more than the stream itself, and so does a
 // grid-wide barrier.  So every workgroup derives the activation split on its
-// own (X is at most 16 x 4096 values and sits in L2 after the first touch):
-//   1. load X in the MFMA operand layout (lane = token row t);
-//   2. statistics with packed 16-bit integer max over |x| bit patterns: a
-//      column is an outlier when some |x| > threshold ("Core idea of
-//      LLM.int8()" step 1); the row absmax over the other columns is SCA
-//      ("Quantization mechanics", absmax bullet); then the loads of its 16
-//      weight rows (all of K) are issued, so the weight stream overlaps the
-//      rest and the X loads never queue behind it;
+// own (X is at most 16 x 4096 values and sits in L2 after the first touch),
+// while its weight rows are already on their way:
+//   1. thread c loads the 8-column chunk c of all 16 token rows (each wave
+//      load is 1 KiB of one row, fully coalesced), then the 16 weight rows of
+//      its block in the MFMA operand layout;
+//   2. a column is an outlier when some |x| > threshold ("Core idea of
+//      LLM.int8()" step 1): the thread holds every row of its columns, so the
+//      flags need no exchange; the row absmax over the other columns is SCA
+//      ("Quantization mechanics", absmax bullet), reduced across the
+//      workgroup with packed 16-bit maxima;
 //   3. codes round(fl32(|x| * fl32(127 / SCA))) with halves away from zero,
-//      signed, 0 on outlier columns, written straight into the MFMA A
-//      operands;
-//   4. v_mfma_i32_16x16x64_i8 over K, the eight waves' int32 tiles summed in
-//      a fixed order, then the epilogue: dequantisation, the 16-bit outlier
-//      product against (CB * SCB) / 127 ("Integration into transformers"),
-//      bias, one rounding.
-// Workgroup 0 also writes the side outputs (CA, SCA, bitmap, idx, n_idx).
+//      signed, 0 on outlier columns, go to LDS row-major (XOR-swizzled);
+//   4. v_mfma_i32_16x16x64_i8 with A read back from LDS, the eight waves'
+//      int32 tiles summed in a fixed order, then the epilogue:
+//      dequantisation, the 16-bit outlier product against (CB * SCB) / 127
+//      ("Integration into transformers"), bias, one rounding.  The outlier
+//      columns' X values and recovered weights come from registers.
+// Side outputs (CA, SCA, bitmap, idx, n_idx) are written by all workgroups
+// together (CA) or by workgroup 0 (the small ones).
 #include "lli8_device.h"
 #include "lli8_internal.h"
 
 namespace lli8 {
 
-constexpr int FD_NW = 8;                      // waves per workgroup: two per SIMD
-constexpr int FD_THREADS = FD_NW * 64;
-constexpr int FD_SS = 2;                      // 256-column K slices per wave
-constexpr int FD_MAXK = FD_NW * FD_SS * 256;  // 4096
-constexpr int FD_MAXW = FD_MAXK / 32;
-constexpr int FD_OUT_LDS = 64;           // outlier columns staged in LDS; more fall back to global reads
+constexpr int FD_CW = 8;                      // activation waves
+constexpr int FD_LW = 4;                      // weight waves
+constexpr int FD_THREADS = (FD_CW + FD_LW) * 64;  // 768: three waves per SIMD
+constexpr int FD_MAXK = FD_CW * 64 * 8;       // 4096: one 8-column chunk per activation thread
+constexpr int FD_MAXW = FD_MAXK / 32;         // bitmap words
+constexpr int FD_MPL = FD_MAXK / FD_LW / 64;  // MFMAs (64 columns each) per weight wave: 16
+constexpr int FD_OUT_LDS = 64;                // outlier columns staged in LDS; more read global memory
 
 // Codes of the two 16-bit values of x for row factor s = fl32(127 / absmax),
-// as two int16 in one dword.  |x| * s <= 127.5, and for such v,
-// round-half-away(v) == floor(fl32(v' + 0.5)) with v' = v with mantissa bit 0
-// cleared (v' + 0.5 is exact, and clearing bit 0 never moves v across a
-// half-integer); v_cvt_rpi_i32_f32 computes floor(v' + 0.5).  The sign of x
-// is applied to both magnitudes at once with packed 16-bit arithmetic.
+// as two int16 in one dword.  v = fl32(|x| * s) <= 127.5 (for fp16 one
+// v_fma_mix_f32 with a zero addend: the same single rounding of the exact
+// product), and round-half-away(v) = floor(v + 0.5) for v >= 0, which
+// v_cvt_rpi_i32_f32 computes.  Its result is the same whether or not the
+// hardware rounds v + 0.5 to fp32 first: the one value where that rounding
+// would reach the next integer, v = 0.5 - 2^-25, is not the product of any
+// fp16 or bf16 value with the scale of any fp16 or bf16 absmax.  The sign of
+// x is applied to both magnitudes at once with packed 16-bit arithmetic.
 typedef short i16x2 __attribute__((ext_vector_type(2)));
+typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
 
 __device__ __forceinline__ int cvt_rpi(float v) {
   int r;
@@ -50,11 +56,17 @@ __device__ __forceinline__ int cvt_rpi(float v) {
 }
 
 template <int DT>
+__device__ __forceinline__ float scaled_abs(uint32_t bits16, float s) {
+  if constexpr (DT == DT_F16)
+    return __builtin_fmaf(__builtin_fabsf((float)__builtin_bit_cast(_Float16, (uint16_t)bits16)), s, 0.0f);
+  else
+    return __uint_as_float((bits16 & 0x7FFFu) << 16) * s;
+}
+
+template <int DT>
 __device__ __forceinline__ uint32_t code_pair16(uint32_t x, float s) {
-  const float vlo = fabsf(to_f32<DT>(x & 0xFFFFu)) * s;
-  const float vhi = fabsf(to_f32<DT>(x >> 16)) * s;
-  const int mlo = cvt_rpi(__uint_as_float(__float_as_uint(vlo) & 0xFFFFFFFEu));
-  const int mhi = cvt_rpi(__uint_as_float(__float_as_uint(vhi) & 0xFFFFFFFEu));
+  const int mlo = cvt_rpi(scaled_abs<DT>(x & 0xFFFFu, s));
+  const int mhi = cvt_rpi(scaled_abs<DT>(x >> 16, s));
   const i16x2 mag = __builtin_bit_cast(i16x2, (uint32_t)mlo | ((uint32_t)mhi << 16));
   const i16x2 neg = __builtin_bit_cast(i16x2, x) >> 15;  // -1 where x < 0
   return __builtin_bit_cast(uint32_t, (i16x2)((mag ^ neg) - neg));
@@ -65,35 +77,86 @@ __device__ __forceinline__ uint32_t pack_codes16(uint32_t p01, uint32_t p23) {
   return __builtin_amdgcn_perm(p23, p01, 0x06040200u);
 }
 
-// Column of the first value of 8-value chunk j (0..7) that lane group g (0..3)
-// holds in 256-column slice s.  Chunks 2u and 2u+1 form MFMA operand u, which
-// covers columns s*256 + 64u + 16g .. +16; the weight operand uses the same
-// columns, so the int8 dot products are exact in any order.  The four lanes
-// of a row then read one 128-byte line per load instruction.
-__device__ __forceinline__ int col_of(int s, int j, int g) { return s * 256 + (j >> 1) * 64 + g * 16 + (j & 1) * 8; }
-
-// 256-column slice behind register slot i of wave w.  Each workgroup starts
-// at a different slice (rot), so the workgroups, which all read the same X,
-// do not walk the same L2 channels in lockstep; the slot -> slice map stays a
-// bijection, and activation and weight operands share it.
-__device__ __forceinline__ int slice_of(int w, int i, int rot, int nss) {
-  const int s = w + FD_NW * i;
-  return s < nss ? (s + rot) % nss : s;
-}
-
-typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
-
 // Larger of each 16-bit half (v_pk_max_u16).
 __device__ __forceinline__ uint32_t pk_max_u16(uint32_t a, uint32_t b) {
   return __builtin_bit_cast(uint32_t, __builtin_elementwise_max(__builtin_bit_cast(u16x2, a), __builtin_bit_cast(u16x2, b)));
 }
 
-// Largest 15-bit magnitude of an 8-value chunk.
-__device__ __forceinline__ uint32_t chunk_max(const u32x4& v) {
-  const uint32_t m2 = pk_max_u16(pk_max_u16(v[0] & 0x7FFF7FFFu, v[1] & 0x7FFF7FFFu),
-                                 pk_max_u16(v[2] & 0x7FFF7FFFu, v[3] & 0x7FFF7FFFu));
-  return max(m2 & 0xFFFFu, m2 >> 16);
+// 0xFF in every byte whose bit is set in the low 4 bits of f.
+__device__ __forceinline__ uint32_t byte_mask4(uint32_t f) {
+  return ((f & 1u) * 0xFFu) | (((f >> 1) & 1u) * 0xFF00u) | (((f >> 2) & 1u) * 0xFF0000u) |
+         (((f >> 3) & 1u) * 0xFF000000u);
 }
+
+// Cross-lane moves without LDS: DPP within a row of 16 lanes, the gfx950
+// permlane swaps across rows.
+template <int CTRL>
+__device__ __forceinline__ uint32_t dpp(uint32_t v) {
+  return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, CTRL, 0xF, 0xF, false);
+}
+constexpr int DPP_QUAD_XOR1 = 0xB1;    // quad_perm [1, 0, 3, 2]
+constexpr int DPP_QUAD_XOR2 = 0x4E;    // quad_perm [2, 3, 0, 1]
+constexpr int DPP_ROW_ROR8 = 0x128;    // lane l <- lane l ^ 8 within its row
+constexpr int DPP_HALF_MIRROR = 0x141;  // lane l <- lane 7 - l within its 8-lane half row
+
+// Packed 16-bit maxima of eight dwords per lane, reduced over the wave.  The
+// result for dword p sits in lanes 8p .. 8p + 7.  Each step halves the data
+// each lane carries: dwords p and p + 4 trade halves of the wave (permlane32
+// swap), then p and p + 2 trade rows (permlane16 swap), then p and p + 1
+// trade half rows, and the last three steps finish within 8 lanes.
+__device__ __forceinline__ uint32_t wave_max8_u16x2(const uint32_t (&pr)[8], int lane) {
+  uint32_t q4[4], q2[2];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const auto r = __builtin_amdgcn_permlane32_swap(pr[i], pr[i + 4], false, false);
+    q4[i] = pk_max_u16(r[0], r[1]);  // lanes 0-31: dword i, lanes 32-63: dword i + 4
+  }
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const auto r = __builtin_amdgcn_permlane16_swap(q4[i], q4[i + 2], false, false);
+    q2[i] = pk_max_u16(r[0], r[1]);  // even rows: dword of q4[i], odd rows: of q4[i + 2]
+  }
+  const bool b3 = (lane & 8) != 0;
+  const uint32_t send = b3 ? q2[0] : q2[1];
+  uint32_t q1 = pk_max_u16(b3 ? q2[1] : q2[0], dpp<DPP_ROW_ROR8>(send));
+  q1 = pk_max_u16(q1, dpp<DPP_HALF_MIRROR>(q1));
+  q1 = pk_max_u16(q1, dpp<DPP_QUAD_XOR1>(q1));
+  q1 = pk_max_u16(q1, dpp<DPP_QUAD_XOR2>(q1));
+  return q1;
+}
+
+// Packed 16-bit maxima over the lanes that share (lane & 7): lane l ^ 8
+// within its row, then across rows and halves of the wave.
+__device__ __forceinline__ uint32_t wave_max_by8_u16x2(uint32_t v) {
+  v = pk_max_u16(v, dpp<DPP_ROW_ROR8>(v));
+  {
+    const auto r = __builtin_amdgcn_permlane16_swap(v, v, false, false);
+    v = pk_max_u16(r[0], r[1]);
+  }
+  {
+    const auto r = __builtin_amdgcn_permlane32_swap(v, v, false, false);
+    v = pk_max_u16(r[0], r[1]);
+  }
+  return v;
+}
+
+// Exclusive prefix counts of outlier bitmap words 2l and 2l + 1 (W <= 128)
+// packed as two 16-bit halves in lane l, and the total count.
+__device__ __forceinline__ uint32_t bitmap_prefix(const uint32_t* s_bm, int W, int lane, int& total) {
+  const uint32_t w0 = (2 * lane < W) ? s_bm[2 * lane] : 0u;
+  const uint32_t w1 = (2 * lane + 1 < W) ? s_bm[2 * lane + 1] : 0u;
+  const int cnt = __popc(w0) + __popc(w1);
+  const int incl = wave_incl_scan(cnt);
+  total = __shfl(incl, 63, WAVE);
+  const uint32_t p0 = (uint32_t)(incl - cnt);
+  return p0 | ((p0 + (uint32_t)__popc(w0)) << 16);
+}
+
+// LDS byte offset of 16-byte code chunk ch (0..255) of token row t.  Rows are
+// FD_MAXK bytes; the XOR gives the 16 rows that one MFMA operand read touches
+// 16 distinct 16-byte bank groups, and keeps the row-wise writes
+// conflict-free.
+__device__ __forceinline__ int code_off(int t, int ch) { return t * FD_MAXK + ((ch ^ t) << 4); }
 
 template <int DT>
 __global__ __launch_bounds__(FD_THREADS, 1) void decode_fused_kernel(
@@ -101,301 +164,302 @@ __global__ __launch_bounds__(FD_THREADS, 1) void decode_fused_kernel(
     const float* __restrict__ SCB, const uint16_t* __restrict__ bias, uint16_t* __restrict__ out,
     int8_t* __restrict__ CA, float* __restrict__ SCA, uint32_t* __restrict__ bitmap,
     int32_t* __restrict__ idx, int32_t* __restrict__ n_idx_out, int32_t* __restrict__ acc_out) {
+  __shared__ __attribute__((aligned(16))) uint8_t s_codes[16 * FD_MAXK];
   __shared__ uint32_t s_bm[FD_MAXW];
   __shared__ uint32_t s_pre[FD_MAXW];
   __shared__ int32_t s_idx[FD_MAXK];
-  __shared__ uint32_t s_rmax[16];
-  __shared__ int s_any;
-  __shared__ v4i s_red[FD_NW - 1][64];
+  __shared__ uint32_t s_wmax[FD_CW][8];  // per activation wave: row maxima, two rows per dword
+  __shared__ uint32_t s_wany[FD_CW];
+  __shared__ float s_sca[16];
+  __shared__ int s_nout;
+  __shared__ v4i s_red[FD_LW - 1][64];
   __shared__ float s_ow[FD_OUT_LDS][16];  // recovered weights of the outlier columns, this block
   __shared__ float s_ox[FD_OUT_LDS][16];  // X values of the outlier columns
 
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-  const int nr = lane & 15, g = lane >> 4;
   const int G = gridDim.x, wg = blockIdx.x;
   const int nblk = (N + 15) >> 4;
-  const int nss = (K + 255) >> 8;
   const int W = (K + 31) >> 5;
-  const int rot = wg % nss;
-
-  // |x| > tau  <=>  (bits & 0x7FFF) > t16, t16 = largest 16-bit magnitude <= tau
-  const bool outl = tau > 0.0f && tau <= 3.4028235e38f;
-  uint32_t t16 = 0xFFFFu;
-  if (outl) {
-    uint32_t bb = from_f32<DT>(tau);
-    if (to_f32<DT>(bb) > tau) bb -= 1u;
-    t16 = bb & 0x7FFFu;
-  }
-
-  for (int i = tid; i < W; i += FD_THREADS) s_bm[i] = 0u;
-  if (tid < 16) s_rmax[tid] = 0u;
-  if (tid == 0) s_any = 0;
-
-  // 1. activations: row nr, chunk j of slot i at column col_of(slice, j, g).
-  // Loads are unconditional, at clamped in-range addresses, so the compiler
-  // counts them in order.  Validity is applied where values are used: chunks
-  // beyond K count as zero; rows beyond T only feed accumulator rows the
-  // epilogue never stores, and never flag a column.
-  const bool row_ok = nr < T;
-  u32x4 xr[FD_SS][8];
-  bool kok[FD_SS][8];
-  {
-    const uint16_t* xrow = X + (int64_t)(row_ok ? nr : 0) * K;
-#pragma unroll
-    for (int i = 0; i < FD_SS; ++i) {
-      const int s = slice_of(w, i, rot, nss);
-#pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        const int k = col_of(s, j, g);
-        kok[i][j] = s < nss && k < K;
-        xr[i][j] = *reinterpret_cast<const u32x4*>(xrow + (kok[i][j] ? k : 0));
-      }
-    }
-  }
   const int blk0 = wg;  // the grid never exceeds the number of blocks
-  float scb_pre = 0.0f, bias_pre = 0.0f;  // first block's scale and bias, epilogue lanes
-  {
-    const int64_t col = (int64_t)blk0 * 16 + (lane & 15);
-    if (w == 0 && col < N) {
-      scb_pre = SCB[col];
-      bias_pre = (bias != nullptr) ? to_f32<DT>(bias[col]) : 0.0f;
-    }
-  }
 
-  // 2. statistics: per-chunk (8 columns) maxima of the 15-bit magnitudes
-  uint32_t cmax[FD_SS][8];
-  uint32_t lmax = 0u;
-  uint32_t hot = 0u;  // bit 8i+j: chunk (i, j) holds a value above the threshold
-#pragma unroll
-  for (int i = 0; i < FD_SS; ++i)
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      cmax[i][j] = kok[i][j] ? chunk_max(xr[i][j]) : 0u;
-      lmax = max(lmax, cmax[i][j]);
-      hot |= (outl && row_ok && cmax[i][j] > t16) ? (1u << (8 * i + j)) : 0u;
+  // Both roles pass the same sequence of workgroup barriers: B1 (per-wave
+  // row maxima, bitmap), B2 (codes, outlier index list, X values and
+  // recovered weights of the outlier columns, row scales), then per block B3
+  // (partial tiles) and B4 (epilogue done).
+  if (w < FD_CW) {
+    // ------------------------------------------------ activation waves ----
+    // |x| > tau  <=>  (bits & 0x7FFF) > t16, t16 = largest 16-bit magnitude <= tau
+    const bool outl = tau > 0.0f && tau <= 3.4028235e38f;
+    uint32_t t16 = 0xFFFFu;
+    if (outl) {
+      uint32_t bb = from_f32<DT>(tau);
+      if (to_f32<DT>(bb) > tau) bb -= 1u;
+      t16 = bb & 0x7FFFu;
     }
-
-  // 3. weight rows of the first block, issued once X has been consumed so the
-  //    activation loads never queue behind the weight stream
-  u32x4 b[FD_SS][4];
-  auto load_cb = [&](int blk) {  // rows beyond N give accumulator columns that are never stored
-    const int64_t n = (int64_t)blk * 16 + nr;
-    const int8_t* brow = CB + (n < N ? n : 0) * K;
+    // 1. chunk c = tid, columns 8c .. 8c + 7, all 16 rows.  Loads are
+    // unconditional at clamped in-range addresses, so the compiler counts them
+    // in order.  Rows beyond T repeat row T - 1 (harmless: they change no
+    // column maximum and only feed accumulator rows that are never stored);
+    // chunks beyond K are masked where their values are used.
+    const int c = tid;
+    const bool cok = 8 * c < K;
+    u32x4 xr[16];
+    {
+      const uint16_t* xc = X + (cok ? 8 * c : 0);
 #pragma unroll
-    for (int i = 0; i < FD_SS; ++i) {
-      const int s = slice_of(w, i, rot, nss);
-#pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        const int k = col_of(s, 2 * u, g);
-        b[i][u] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(brow + ((s < nss && k < K) ? k : 0)));
+      for (int t = 0; t < 16; ++t) {
+        const int tt = t < T ? t : T - 1;
+        xr[t] = *reinterpret_cast<const u32x4*>(xc + (int64_t)tt * K);
       }
     }
-  };
-  __builtin_amdgcn_sched_barrier(0);
-  load_cb(blk0);
-  __builtin_amdgcn_sched_barrier(0);
 
-  // 4. outlier columns: OR of the hot-chunk masks over the wave, then only
-  //    the hot chunks are examined value by value
-  uint32_t hw = hot;
+    // 2. statistics: column maxima of the 15-bit magnitudes over the 16 rows
+    // (two columns per dword) and, in the same pass, each row's maximum over
+    // this chunk.
+    uint32_t cm[4] = {0u, 0u, 0u, 0u};
+    uint32_t rm[16];
 #pragma unroll
-  for (int off = 1; off < 64; off <<= 1) hw |= (uint32_t)__shfl_xor((int)hw, off, WAVE);
-  __syncthreads();  // LDS initialised
-  if (lane == 0 && hw) s_any = 1;
-  __syncthreads();
-  const bool any = s_any != 0;
-  bool mine = false;  // does this lane's column set hold an outlier column?
-  if (any) {
+    for (int t = 0; t < 16; ++t) {
+      uint32_t a[4];
 #pragma unroll
-    for (int i = 0; i < FD_SS; ++i)
+      for (int d = 0; d < 4; ++d) {
+        a[d] = xr[t][d] & 0x7FFF7FFFu;
+        cm[d] = pk_max_u16(cm[d], a[d]);
+      }
+      rm[t] = pk_max_u16(pk_max_u16(a[0], a[1]), pk_max_u16(a[2], a[3]));
+    }
+    uint32_t f8 = 0u;  // bit e: column 8c + e is an outlier column
 #pragma unroll
-      for (int j = 0; j < 8; ++j)
-        if ((hw >> (8 * i + j)) & 1u) {  // wave-uniform
-          uint32_t bits = 0u;
-          if ((hot >> (8 * i + j)) & 1u) {
+    for (int d = 0; d < 4; ++d)
+      f8 |= (((cm[d] & 0xFFFFu) > t16) ? (1u << (2 * d)) : 0u) | (((cm[d] >> 16) > t16) ? (2u << (2 * d)) : 0u);
+    f8 = cok ? f8 : 0u;
+    {  // bitmap word c / 4 from the four lanes of a quad; no atomics
+      uint32_t wv = f8 << (8 * (c & 3));
+      wv |= dpp<DPP_QUAD_XOR1>(wv);
+      wv |= dpp<DPP_QUAD_XOR2>(wv);
+      if ((c & 3) == 0 && cok) s_bm[c >> 2] = wv;
+    }
+    const uint64_t anyw = __ballot(f8 != 0u);
+    if (lane == 0) s_wany[w] = anyw != 0 ? 1u : 0u;
+    if (!cok) {
 #pragma unroll
-            for (int e = 0; e < 8; ++e) bits |= ((half_bits(xr[i][j], e) & 0x7FFFu) > t16 ? 1u : 0u) << e;
+      for (int t = 0; t < 16; ++t) rm[t] = 0u;
+    }
+    if (f8 != 0u) {  // rare: leave this chunk's outlier columns out of the row maxima
+      uint32_t km[4];
+#pragma unroll
+      for (int d = 0; d < 4; ++d)
+        km[d] = ((((f8 >> (2 * d)) & 1u) ? 0u : 0x7FFFu) | (((f8 >> (2 * d + 1)) & 1u) ? 0u : 0x7FFF0000u));
+#pragma unroll
+      for (int t = 0; t < 16; ++t) {
+        const u32x4& v = xr[t];
+        rm[t] = pk_max_u16(pk_max_u16(v[0] & km[0], v[1] & km[1]), pk_max_u16(v[2] & km[2], v[3] & km[3]));
+      }
+    }
+    {  // two rows per dword, then over the wave: lanes 8p .. 8p + 7 get rows 2p, 2p + 1
+      uint32_t pr[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i)
+        pr[i] = pk_max_u16(__builtin_amdgcn_perm(rm[2 * i + 1], rm[2 * i], 0x05040100u),
+                           __builtin_amdgcn_perm(rm[2 * i + 1], rm[2 * i], 0x07060302u));
+      const uint32_t q1 = wave_max8_u16x2(pr, lane);
+      if ((lane & 7) == 0) s_wmax[w][lane >> 3] = q1;
+    }
+    __syncthreads();  // B1
+
+    // row scales, in every wave: lane l takes rows 2p, 2p + 1 with p = l & 7
+    const bool any = __ballot(lane < FD_CW && s_wany[lane & (FD_CW - 1)] != 0u) != 0;
+    const uint32_t rmax2 = wave_max_by8_u16x2(s_wmax[lane >> 3][lane & 7]);
+    const float sca_lo = to_f32<DT>(rmax2 & 0xFFFFu), sca_hi = to_f32<DT>(rmax2 >> 16);  // exact row absmax
+    const float sf_lo = (sca_lo > 0.0f) ? 127.0f / sca_lo : 0.0f;
+    const float sf_hi = (sca_hi > 0.0f) ? 127.0f / sca_hi : 0.0f;
+    if (w == 0 && lane < 8) {
+      s_sca[2 * lane] = sca_lo;
+      s_sca[2 * lane + 1] = sca_hi;
+    }
+
+    // 3. codes into LDS
+    {
+      const uint32_t ok = cok ? 0xFFFFFFFFu : 0u;  // chunks beyond K get zero codes
+      const uint32_t z0 = ~byte_mask4(f8) & ok, z1 = ~byte_mask4(f8 >> 4) & ok;  // and outlier columns
+#pragma unroll
+      for (int t = 0; t < 16; ++t) {
+        const float sf = __builtin_bit_cast(float, __builtin_amdgcn_readlane(
+            __builtin_bit_cast(int, (t & 1) ? sf_hi : sf_lo), t >> 1));
+        const u32x4& v = xr[t];
+        u32x2 cw;
+        cw[0] = pack_codes16(code_pair16<DT>(v[0], sf), code_pair16<DT>(v[1], sf)) & z0;
+        cw[1] = pack_codes16(code_pair16<DT>(v[2], sf), code_pair16<DT>(v[3], sf)) & z1;
+        *reinterpret_cast<u32x2*>(&s_codes[code_off(t, c >> 1) + (c & 1) * 8]) = cw;
+      }
+    }
+    int n_out = 0;
+    if (any) {  // this chunk's outlier columns: their index and X values
+      const uint32_t pp = bitmap_prefix(s_bm, W, lane, n_out);
+      const int word = c >> 2;  // prefix of this chunk's bitmap word, from lane word / 2 of this wave
+      const uint32_t pw = (uint32_t)__shfl((int)pp, (word >> 1) & 63, WAVE);
+      const uint32_t pre = (word & 1) ? (pw >> 16) : (pw & 0xFFFFu);
+      uint32_t f = f8;
+      while (f) {
+        const int e = __builtin_ctz(f);
+        f &= f - 1u;
+        const int col = 8 * c + e;
+        const int rank = (int)pre + __popc(s_bm[word] & ((1u << (col & 31)) - 1u));
+        s_idx[rank] = col;
+        if (rank < FD_OUT_LDS) {
+#pragma unroll
+          for (int t = 0; t < 16; ++t) s_ox[rank][t] = (t < T) ? to_f32<DT>(half_bits(xr[t], e)) : 0.0f;
+        }
+      }
+    }
+    __syncthreads();  // B2
+
+    // side outputs: CA shared out over the grid, the small ones by workgroup 0
+    {
+      const int cpr = K >> 4;  // 16-byte code chunks per row
+      const int units = T * cpr;
+      for (int u = wg + G * tid; u < units; u += G * (FD_CW * 64)) {
+        const int t = u / cpr, ch = u - t * cpr;
+        *reinterpret_cast<v4i*>(CA + (int64_t)t * K + ch * 16) = *reinterpret_cast<const v4i*>(&s_codes[code_off(t, ch)]);
+      }
+    }
+    if (wg == 0) {
+      if (tid < T) SCA[tid] = s_sca[tid];
+      for (int i = tid; i < W; i += FD_CW * 64) bitmap[i] = s_bm[i];
+      for (int p = tid; p < n_out; p += FD_CW * 64) idx[p] = s_idx[p];
+      if (tid == 0) *n_idx_out = n_out;
+    }
+    for (int blk = blk0; blk < nblk; blk += G) {
+      __syncthreads();  // B3
+      __syncthreads();  // B4
+    }
+  } else {
+    // ---------------------------------------------------- weight waves ----
+    // Their loads may wait for queue space in the memory pipeline for as long
+    // as the weight stream takes; no other work waits behind them.
+    const int lw = w - FD_CW;
+    const int nr = lane & 15, q = lane >> 4;
+    // weight rows of a block in the MFMA B layout: lane (n, q) of weight wave
+    // lw holds CB[n][k0 .. k0 + 16) for k0 = 1024 lw + 64 m + 16 q, m = 0 ..
+    // 15.  Buffer loads over the block's rows: a read past the last row of CB
+    // returns zeros, and reads past K within a row only meet zero codes.
+    u32x4 b[FD_MPL];
+    float scb_n, bias_n;  // scale and bias of feature nr of the block
+    const int vo = nr * K + lw * 1024 + q * 16;
+    auto load_cb = [&](int blk) {
+      const int rows = min(16, N - blk * 16);
+      const __amdgpu_buffer_rsrc_t rs =
+          __builtin_amdgcn_make_buffer_rsrc((void*)(CB + (int64_t)blk * 16 * K), 0, rows * K, 0x00020000);
+#pragma unroll
+      for (int m = 0; m < FD_MPL; ++m)
+        b[m] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, vo + m * 64, 0, 2));
+      // unconditional loads at in-range addresses (a branch around them would
+      // make the compiler wait for every load in flight); with no bias the
+      // load reads SCB and is discarded
+      const int64_t n = (int64_t)blk * 16 + nr;
+      const int64_t cc = n < N ? n : (int64_t)N - 1;
+      const uint16_t* bsrc = (bias != nullptr) ? bias : reinterpret_cast<const uint16_t*>(SCB);
+      const uint32_t bmask = (bias != nullptr) ? 0xFFFFu : 0u;
+      scb_n = SCB[cc];
+      bias_n = to_f32<DT>(bsrc[cc] & bmask);
+    };
+    // recovered weights dtype(fl32(fl32(CB * SCB) / 127)) of the outlier
+    // columns of this block, from registers
+    auto stage_outlier_weights = [&](uint32_t pp) {
+#pragma unroll
+      for (int m = 0; m < FD_MPL; ++m) {
+        const int k0 = lw * 1024 + m * 64 + q * 16;
+        const int word = k0 >> 5;
+        uint32_t bits = (k0 < K) ? (s_bm[word] >> (k0 & 31)) & 0xFFFFu : 0u;
+        if (__ballot(bits != 0u) == 0) continue;  // no outlier column among these 64
+        const uint32_t pw = (uint32_t)__builtin_amdgcn_readlane((int)pp, lw * 16 + m);  // = word / 2
+        const uint32_t pre = (word & 1) ? (pw >> 16) : (pw & 0xFFFFu);
+        while (bits) {
+          const int e = __builtin_ctz(bits);
+          bits &= bits - 1u;
+          const int col = k0 + e;
+          const int rank = (int)pre + __popc(s_bm[word] & ((1u << (col & 31)) - 1u));
+          if (rank < FD_OUT_LDS) {
+            const int8_t cb = (int8_t)((b[m][e >> 2] >> (8 * (e & 3))) & 0xFFu);
+            s_ow[rank][nr] = to_f32<DT>(from_f32<DT>(((float)cb * scb_n) / 127.0f));
           }
-          // the 16 lanes of a group hold the same columns for 16 rows
-          bits |= __shfl_xor(bits, 1, WAVE);
-          bits |= __shfl_xor(bits, 2, WAVE);
-          bits |= __shfl_xor(bits, 4, WAVE);
-          bits |= __shfl_xor(bits, 8, WAVE);
-          const int col = col_of(slice_of(w, i, rot, nss), j, g);
-          if (nr == 0 && bits) atomicOr(&s_bm[col >> 5], bits << (col & 31));
-        }
-    __syncthreads();
-    uint32_t fl[FD_SS][4];  // flag bits of the 16 columns behind operand u
-#pragma unroll
-    for (int i = 0; i < FD_SS; ++i) {
-      const int s = slice_of(w, i, rot, nss);
-#pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        const int c0 = col_of(s, 2 * u, g);
-        fl[i][u] = (s < nss && c0 < K) ? (s_bm[c0 >> 5] >> (c0 & 31)) & 0xFFFFu : 0u;
-        mine |= fl[i][u] != 0u;
-      }
-    }
-    if (mine) {  // row maximum without the outlier columns
-      lmax = 0u;
-#pragma unroll
-      for (int i = 0; i < FD_SS; ++i)
-#pragma unroll
-        for (int j = 0; j < 8; ++j) {
-          const uint32_t f8 = (fl[i][j >> 1] >> (8 * (j & 1))) & 0xFFu;
-          uint32_t cm = cmax[i][j];
-          if (f8 != 0u) {
-            cm = 0u;
-#pragma unroll
-            for (int e = 0; e < 8; ++e)
-              cm = max(cm, ((f8 >> e) & 1u) ? 0u : (half_bits(xr[i][j], e) & 0x7FFFu));
-          }
-          lmax = max(lmax, cm);
-        }
-    }
-  }
-  lmax = max(lmax, (uint32_t)__shfl_xor((int)lmax, 16, WAVE));
-  lmax = max(lmax, (uint32_t)__shfl_xor((int)lmax, 32, WAVE));
-  if (g == 0) atomicMax(&s_rmax[nr], lmax);
-  __syncthreads();
-  const float sca = to_f32<DT>(s_rmax[nr]);  // exact row absmax over non-outlier columns
-  const float sf = (sca > 0.0f) ? 127.0f / sca : 0.0f;
-
-  // 5. codes, straight into the MFMA A operands: a[i][u] = columns col_of(slice, 2u, g) .. +16
-  u32x4 a[FD_SS][4];
-#pragma unroll
-  for (int i = 0; i < FD_SS; ++i)
-#pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      u32x4 r;
-#pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        const u32x4 v = xr[i][2 * u + h];
-        r[2 * h] = pack_codes16(code_pair16<DT>(v[0], sf), code_pair16<DT>(v[1], sf));
-        r[2 * h + 1] = pack_codes16(code_pair16<DT>(v[2], sf), code_pair16<DT>(v[3], sf));
-      }
-      const int c0 = col_of(slice_of(w, i, rot, nss), 2 * u, g);
-      const uint32_t bits16 = (mine && c0 < K) ? (s_bm[c0 >> 5] >> (c0 & 31)) & 0xFFFFu : 0u;
-      if (bits16) {  // zero the codes of outlier columns
-#pragma unroll
-        for (int d = 0; d < 4; ++d) {
-          const uint32_t nib = (bits16 >> (4 * d)) & 0xFu;
-          const uint32_t mask = ((nib & 1u) * 0xFFu) | (((nib >> 1) & 1u) * 0xFF00u) |
-                                (((nib >> 2) & 1u) * 0xFF0000u) | (((nib >> 3) & 1u) * 0xFF000000u);
-          r[d] &= ~mask;
         }
       }
-      a[i][u] = kok[i][2 * u] ? r : (u32x4){0u, 0u, 0u, 0u};  // zero codes beyond K
+    };
+    // The weight loads are issued after B1: a wave issuing them stalls until
+    // queue space frees up, and B1 must not wait for that.  By then the
+    // activation loads have all returned.
+    __syncthreads();  // B1
+    load_cb(blk0);
+    const bool any = __ballot(lane < FD_CW && s_wany[lane & (FD_CW - 1)] != 0u) != 0;
+    int n_out = 0;
+    uint32_t pp = 0u;
+    if (any) {
+      pp = bitmap_prefix(s_bm, W, lane, n_out);
+      stage_outlier_weights(pp);
     }
+    const int n_lds = min(n_out, FD_OUT_LDS);
+    __syncthreads();  // B2
 
-  // side outputs, workgroup 0
-  if (wg == 0) {
-    if (row_ok) {
-#pragma unroll
-      for (int i = 0; i < FD_SS; ++i) {
-        const int s = slice_of(w, i, rot, nss);
-#pragma unroll
-        for (int u = 0; u < 4; ++u) {
-          const int k = col_of(s, 2 * u, g);
-          if (s < nss && k < K) *reinterpret_cast<u32x4*>(CA + (int64_t)nr * K + k) = a[i][u];
-        }
+    // 4. int8 products and epilogue, 16 output features at a time
+    for (int blk = blk0; blk < nblk; blk += G) {
+      if (blk != blk0) {
+        load_cb(blk);
+        if (any) stage_outlier_weights(pp);
       }
-    }
-    if (w == 0 && g == 0 && row_ok) SCA[nr] = sca;
-    for (int i = tid; i < W; i += FD_THREADS) bitmap[i] = s_bm[i];
-  }
-  int n_out = 0;
-  if (any) {
-    if (tid < 64) {
-      const int seg = (W + 63) / 64;
-      const int w0 = lane * seg, w1 = min(W, w0 + seg);
-      int cnt = 0;
-      for (int i = w0; i < w1; ++i) cnt += __popc(s_bm[i]);
-      int run = wave_incl_scan(cnt) - cnt;
-      for (int i = w0; i < w1; ++i) {
-        s_pre[i] = (uint32_t)run;
-        run += __popc(s_bm[i]);
-      }
-    }
-    __syncthreads();
-    n_out = (int)(s_pre[W - 1] + __popc(s_bm[W - 1]));
-    for (int i = tid; i < W; i += FD_THREADS) {
-      uint32_t m = s_bm[i];
-      int pos = (int)s_pre[i];
-      while (m) {
-        const int bit = __builtin_ctz(m);
-        s_idx[pos] = i * 32 + bit;
-        if (wg == 0) idx[pos] = i * 32 + bit;
-        ++pos;
-        m &= m - 1u;
-      }
-    }
-    __syncthreads();
-  }
-  if (wg == 0 && tid == 0) *n_idx_out = n_out;
-
-  // X values of the outlier columns (the same for every block)
-  const int n_lds = min(n_out, FD_OUT_LDS);
-  for (int q = tid; q < n_lds * 16; q += FD_THREADS) {
-    const int p = q >> 4, t = q & 15;
-    s_ox[p][t] = (t < T) ? to_f32<DT>(X[(int64_t)t * K + s_idx[p]]) : 0.0f;
-  }
-
-  // 6. int8 products and epilogue, 16 output features at a time
-  for (int blk = blk0; blk < nblk; blk += G) {
-    if (blk != blk0) load_cb(blk);
-    // recovered weights dtype(fl32(fl32(CB * SCB) / 127)) of the outlier columns, all loads in parallel
-    for (int q = tid; q < n_lds * 16; q += FD_THREADS) {
-      const int p = q >> 4;
-      const int64_t col = (int64_t)blk * 16 + (q & 15);
-      float wv = 0.0f;
-      if (col < N) wv = to_f32<DT>(from_f32<DT>(((float)CB[col * K + s_idx[p]] * SCB[col]) / 127.0f));
-      s_ow[p][q & 15] = wv;
-    }
-    v4i acc = {0, 0, 0, 0};
-#pragma unroll
-    for (int i = 0; i < FD_SS; ++i)
-#pragma unroll
-      for (int u = 0; u < 4; ++u)
-        acc = __builtin_amdgcn_mfma_i32_16x16x64_i8(__builtin_bit_cast(v4i, a[i][u]), __builtin_bit_cast(v4i, b[i][u]),
-                                                    acc, 0, 0, 0);
-    if (w > 0) s_red[w - 1][lane] = acc;
-    __syncthreads();
-    if (w == 0) {
-#pragma unroll
-      for (int q = 0; q < FD_NW - 1; ++q) acc += s_red[q][lane];  // fixed order: deterministic
-      // 16x16 layout: lane holds feature lane % 16, tokens 4 * (lane / 16) + r
-      const int64_t col = (int64_t)blk * 16 + (lane & 15);
-      if (col < N) {
-        const float scb = (blk == blk0) ? scb_pre : SCB[col];
-        const float bv = (blk == blk0) ? bias_pre : ((bias != nullptr) ? to_f32<DT>(bias[col]) : 0.0f);
-        float o[4] = {0.f, 0.f, 0.f, 0.f};
+      // 16-bit outlier product (weight wave 0): for the first block the staged
+      // weights are complete since B2, so it overlaps the int8 products; for
+      // later blocks the other waves stage theirs after B4, so it waits for B3
+      float o[4] = {0.f, 0.f, 0.f, 0.f};
+      auto outlier_sum = [&]() {
         for (int p = 0; p < n_lds; ++p) {
-          const float wv = s_ow[p][lane & 15];
+          const float wv = s_ow[p][nr];
 #pragma unroll
-          for (int r = 0; r < 4; ++r) o[r] += s_ox[p][4 * (lane >> 4) + r] * wv;
+          for (int r = 0; r < 4; ++r) o[r] += s_ox[p][4 * q + r] * wv;
         }
-        for (int p = n_lds; p < n_out; ++p) {  // beyond the LDS stage: straight from memory
-          const int c = s_idx[p];
-          const float wv = to_f32<DT>(from_f32<DT>(((float)CB[col * K + c] * scb) / 127.0f));
+      };
+      if (lw == 0 && blk == blk0) outlier_sum();
+      v4i acc = {0, 0, 0, 0};
+#pragma unroll
+      for (int h = 0; h < FD_MPL; h += 8) {  // A operands (codes of rows 0-15, the same columns), 8 reads in flight
+        v4i am[8];
+#pragma unroll
+        for (int m = 0; m < 8; ++m) am[m] = *reinterpret_cast<const v4i*>(&s_codes[code_off(nr, lw * 64 + (h + m) * 4 + q)]);
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int m = 0; m < 8; ++m)
+          acc = __builtin_amdgcn_mfma_i32_16x16x64_i8(am[m], __builtin_bit_cast(v4i, b[h + m]), acc, 0, 0, 0);
+      }
+      if (lw > 0) s_red[lw - 1][lane] = acc;
+      __syncthreads();  // B3
+      if (lw == 0) {
+        if (blk != blk0) outlier_sum();
+#pragma unroll
+        for (int i = 0; i < FD_LW - 1; ++i) acc += s_red[i][lane];  // fixed order: deterministic
+        // 16x16 layout: lane holds feature lane % 16, tokens 4 * (lane / 16) + r
+        const int64_t col = (int64_t)blk * 16 + nr;
+        if (col < N) {
+          for (int p = n_lds; p < n_out; ++p) {  // beyond the LDS stage: straight from memory
+            const int cc = s_idx[p];
+            const float wv = to_f32<DT>(from_f32<DT>(((float)CB[col * K + cc] * scb_n) / 127.0f));
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+              const int t = 4 * q + r;
+              if (t < T) o[r] += to_f32<DT>(X[(int64_t)t * K + cc]) * wv;
+            }
+          }
 #pragma unroll
           for (int r = 0; r < 4; ++r) {
-            const int t = 4 * (lane >> 4) + r;
-            if (t < T) o[r] += to_f32<DT>(X[(int64_t)t * K + c]) * wv;
+            const int t = 4 * q + r;
+            if (t >= T) continue;
+            if (acc_out != nullptr) acc_out[(int64_t)t * N + col] = acc[r];
+            const float d = (float)acc[r] * (s_sca[t] * (scb_n * (1.0f / 16129.0f)));
+            out[(int64_t)t * N + col] = from_f32<DT>(d + o[r] + bias_n);
           }
         }
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int t = 4 * (lane >> 4) + r;
-          if (t >= T) continue;
-          if (acc_out != nullptr) acc_out[(int64_t)t * N + col] = acc[r];
-          const float sa = to_f32<DT>(s_rmax[t]);
-          const float d = (float)acc[r] * (sa * (scb * (1.0f / 16129.0f)));
-          out[(int64_t)t * N + col] = from_f32<DT>(d + o[r] + bv);
-        }
       }
+      __syncthreads();  // B4
     }
-    __syncthreads();
   }
 }
 
