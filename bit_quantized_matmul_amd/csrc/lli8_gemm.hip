@@ -9,8 +9,10 @@
 // transformers") and the two results are summed.
 //
 // Two kernels:
-//   * tile kernel: BM x BN output tile per 256-thread workgroup (2 x 2
-//     waves), K staged through LDS 64 bytes at a time, double buffered, with
+//   * tile kernel: BM x BN output tile per workgroup of WGM x WGN waves
+//     (256 x 256 on 4 x 2 waves: two waves per SIMD, so one wave's LDS and
+//     barrier waits overlap the other's MFMAs), K staged through LDS 64 bytes
+//     at a time, double buffered, with
 //     v_mfma_i32_32x32x32_i8.  The epilogue turns the int32 accumulators into
 //     fp32 in place (same 32x32 register layout), then runs the outlier
 //     columns through v_mfma_f32_32x32x16_{f16,bf16} on the same registers,
@@ -22,6 +24,7 @@
 #include "lli8_internal.h"
 
 namespace lli8 {
+
 
 // LDS address of 16-byte chunk c of row r in a tile with KB-byte rows.  A
 // 16-byte-per-lane LDS access is served 16 lanes (256 bytes, all 64 banks) at
@@ -69,22 +72,25 @@ __device__ __forceinline__ void tile_coords(int b, int tiles_m, int tiles_n, int
   tn = in / gsz;
 }
 
-template <int DT, int BM, int BN, int KM, int BK>
-__global__ __launch_bounds__(256, 1) void linear_tile_kernel(
+template <int DT, int BM, int BN, int KM, int BK, int WGM, int WGN>
+__global__ __launch_bounds__(64 * WGM * WGN) void linear_tile_kernel(
     const int8_t* __restrict__ CA, const int8_t* __restrict__ CB, const float* __restrict__ SCA,
     const float* __restrict__ SCB, const uint16_t* __restrict__ bias, const uint16_t* __restrict__ xo,
     const int32_t* __restrict__ idx, const int32_t* __restrict__ n_idx_p, uint16_t* __restrict__ out,
     int32_t* __restrict__ acc_out, int T, int N, int K, int tiles_m, int tiles_n) {
-  constexpr int WM = BM / 2, WN = BN / 2;
+  constexpr int NT = 64 * WGM * WGN;                    // threads: WGM x WGN waves
+  constexpr int WM = BM / WGM, WN = BN / WGN;
   constexpr int FM = WM / 32, FN = WN / 32;
   constexpr int CPR = BK / 16;                          // 16-byte chunks per tile row
   constexpr int SS = BK / 32;                           // MFMA sub-steps per K step
-  constexpr int LA = BM * CPR / 256, LB = BN * CPR / 256;  // 16-byte chunks per thread per step
+  constexpr int LA = BM * CPR / NT, LB = BN * CPR / NT;  // 16-byte chunks per thread per step
+  static_assert(LA * NT == BM * CPR && LB * NT == BN * CPR, "tile rows must split evenly over the threads");
+  static_assert(BK == 64 || (BM * 4) % NT == 0, "outlier staging reuses the 64-byte tile rows");
   __shared__ __attribute__((aligned(16))) int8_t sA[2][BM * BK];
   __shared__ __attribute__((aligned(16))) int8_t sB[2][BN * BK];
 
   const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
-  const int wm = wid >> 1, wn = wid & 1;
+  const int wm = wid / WGN, wn = wid % WGN;
   int tm, tn;
   tile_coords<8>(blockIdx.x, tiles_m, tiles_n, tm, tn);
   const int64_t m0 = (int64_t)tm * BM, n0 = (int64_t)tn * BN;
@@ -109,13 +115,13 @@ __global__ __launch_bounds__(256, 1) void linear_tile_kernel(
   const int8_t* pb[LB];
 #pragma unroll
   for (int i = 0; i < LA; ++i) {
-    const int r = (tid + 256 * i) / CPR;
+    const int r = (tid + NT * i) / CPR;
     const int64_t row = m0 + r < T ? m0 + r : (int64_t)T - 1;
     pa[i] = CA + row * K;
   }
 #pragma unroll
   for (int i = 0; i < LB; ++i) {
-    const int r = (tid + 256 * i) / CPR;
+    const int r = (tid + NT * i) / CPR;
     const int64_t row = n0 + r < N ? n0 + r : (int64_t)N - 1;
     pb[i] = CB + row * K;
   }
@@ -155,12 +161,12 @@ __global__ __launch_bounds__(256, 1) void linear_tile_kernel(
   auto lstore = [&](int buf, const u32x4 (&ra)[LA], const u32x4 (&rb)[LB]) {
 #pragma unroll
     for (int i = 0; i < LA; ++i) {
-      const int q = tid + 256 * i, r = q / CPR, c = q % CPR;
+      const int q = tid + NT * i, r = q / CPR, c = q % CPR;
       *reinterpret_cast<u32x4*>(&sA[buf][tile_off<BK>(r, c)]) = ra[i];
     }
 #pragma unroll
     for (int i = 0; i < LB; ++i) {
-      const int q = tid + 256 * i, r = q / CPR, c = q % CPR;
+      const int q = tid + NT * i, r = q / CPR, c = q % CPR;
       *reinterpret_cast<u32x4*>(&sB[buf][tile_off<BK>(r, c)]) = rb[i];
     }
   };
@@ -284,8 +290,8 @@ __global__ __launch_bounds__(256, 1) void linear_tile_kernel(
   for (int ch = 0; ch < n_chunks; ++ch) {
     __syncthreads();
 #pragma unroll
-    for (int i = 0; i < LA; ++i) {
-      const int q = tid + 256 * i, r = q >> 2, c = q & 3;
+    for (int i = 0; i < BM * 4 / NT; ++i) {
+      const int q = tid + NT * i, r = q >> 2, c = q & 3;
       u32x4 v = {0u, 0u, 0u, 0u};
       if (m0 + r < T) v = *reinterpret_cast<const u32x4*>(xo + (((int64_t)ch * T + m0 + r) * 32 + c * 8));
       *reinterpret_cast<u32x4*>(oA + lds_off(r, c)) = v;
@@ -295,7 +301,7 @@ __global__ __launch_bounds__(256, 1) void linear_tile_kernel(
       const int p = ch * 32 + j;
       const bool valid = p < n_idx;
       const int64_t col = valid ? idx[p] : 0;
-      for (int rr = tid >> 5; rr < BN; rr += 8) {
+      for (int rr = tid >> 5; rr < BN; rr += NT / 32) {
         const int64_t gn = n0 + rr;
         uint16_t w = 0;
         if (valid && gn < N) w = recover_w<DT>(CB[gn * K + col], SCB[gn]);
@@ -410,14 +416,14 @@ __global__ __launch_bounds__(256) void linear_decode_kernel(
   }
 }
 
-template <int DT, int BM, int BN, int BK>
+template <int DT, int BM, int BN, int BK, int WGM, int WGN>
 static hipError_t launch_tile(const LinearArgs& a, hipStream_t s) {
   const int tiles_m = (int)((a.T + BM - 1) / BM), tiles_n = (int)((a.N + BN - 1) / BN);
   const int nb = tiles_m * tiles_n;
-  auto k = (a.K % BK) == 0 ? linear_tile_kernel<DT, BM, BN, 0, BK>
-           : (a.K % 16) == 0 ? linear_tile_kernel<DT, BM, BN, 1, BK>
-                             : linear_tile_kernel<DT, BM, BN, 2, BK>;
-  k<<<dim3(nb), dim3(256), 0, s>>>(a.CA, a.CB, a.SCA, a.SCB, static_cast<const uint16_t*>(a.bias),
+  auto k = (a.K % BK) == 0 ? linear_tile_kernel<DT, BM, BN, 0, BK, WGM, WGN>
+           : (a.K % 16) == 0 ? linear_tile_kernel<DT, BM, BN, 1, BK, WGM, WGN>
+                             : linear_tile_kernel<DT, BM, BN, 2, BK, WGM, WGN>;
+  k<<<dim3(nb), dim3(64 * WGM * WGN), 0, s>>>(a.CA, a.CB, a.SCA, a.SCB, static_cast<const uint16_t*>(a.bias),
                                    static_cast<const uint16_t*>(a.xo), a.idx, a.n_idx,
                                    static_cast<uint16_t*>(a.out), a.acc, (int)a.T, (int)a.N, (int)a.K,
                                    tiles_m, tiles_n);
@@ -433,8 +439,8 @@ static hipError_t launch_linear_t(const LinearArgs& a, hipStream_t s) {
         a.idx, a.n_idx, static_cast<uint16_t*>(a.out), a.acc, (int)a.T, (int)a.N, (int)a.K);
     return hipGetLastError();
   }
-  if (a.T >= 512 && a.N >= 512) return launch_tile<DT, 256, 256, 64>(a, s);
-  return launch_tile<DT, 128, 128, 64>(a, s);
+  if (a.T >= 512 && a.N >= 512) return launch_tile<DT, 256, 256, 64, 4, 2>(a, s);
+  return launch_tile<DT, 128, 128, 64, 2, 2>(a, s);
 }
 
 hipError_t launch_linear_gemm(const LinearArgs& a, hipStream_t s) {
