@@ -11,8 +11,11 @@
 // Two kernels:
 //   * tile kernel: BM x BN output tile per workgroup of WGM x WGN waves
 //     (256 x 256 on 4 x 2 waves: two waves per SIMD, so one wave's LDS and
-//     barrier waits overlap the other's MFMAs), K staged through LDS 64 bytes
-//     at a time, double buffered, with
+//     barrier waits overlap the other's MFMAs).  K is staged through LDS:
+//     for the large tiles with global_load_lds straight from memory into a
+//     ring of LDS slots (128-byte steps, two slots, so every row read is a
+//     whole cache line; 64-byte steps in four slots when K % 128 != 0),
+//     otherwise through registers 64 bytes at a time, double buffered, with
 //     v_mfma_i32_32x32x32_i8.  The epilogue turns the int32 accumulators into
 //     fp32 in place (same 32x32 register layout), then runs the outlier
 //     columns through v_mfma_f32_32x32x16_{f16,bf16} on the same registers,
@@ -72,7 +75,24 @@ __device__ __forceinline__ void tile_coords(int b, int tiles_m, int tiles_n, int
   tn = in / gsz;
 }
 
-template <int DT, int BM, int BN, int KM, int BK, int WGM, int WGN>
+// s_waitcnt with only the vector-memory count constrained: at most N of this
+// wave's vector memory operations still outstanding.
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
+}
+
+// 16 bytes per lane from global memory straight into LDS: lane l writes
+// bytes 16 l .. 16 l + 15 after the wave-uniform LDS address `lds`.
+__device__ __forceinline__ void load_lds16(const int8_t* g, int8_t* lds) {
+  __builtin_amdgcn_global_load_lds(g, (__attribute__((address_space(3))) void*)lds, 16, 0, 0);
+}
+
+// DL = 0: global loads staged through registers, LDS double buffered (any K).
+// DL = D >= 3 (K % 64 == 0 only): loads go straight from global memory into a
+// D-stage LDS ring, D - 1 steps ahead.
+template <int DT, int BM, int BN, int KM, int BK, int WGM, int WGN, int GM, int DL>
 __global__ __launch_bounds__(64 * WGM * WGN) void linear_tile_kernel(
     const int8_t* __restrict__ CA, const int8_t* __restrict__ CB, const float* __restrict__ SCA,
     const float* __restrict__ SCB, const uint16_t* __restrict__ bias, const uint16_t* __restrict__ xo,
@@ -86,13 +106,25 @@ __global__ __launch_bounds__(64 * WGM * WGN) void linear_tile_kernel(
   constexpr int LA = BM * CPR / NT, LB = BN * CPR / NT;  // 16-byte chunks per thread per step
   static_assert(LA * NT == BM * CPR && LB * NT == BN * CPR, "tile rows must split evenly over the threads");
   static_assert(BK == 64 || (BM * 4) % NT == 0, "outlier staging reuses the 64-byte tile rows");
-  __shared__ __attribute__((aligned(16))) int8_t sA[2][BM * BK];
-  __shared__ __attribute__((aligned(16))) int8_t sB[2][BN * BK];
+  static_assert(DL == 0 || (DL >= 2 && DL <= 4 && KM == 0), "direct loads: K a multiple of the step");
+  // register-staged loads: one double-buffered array each; direct loads: one
+  // LDS object per ring slot (slots beyond DL are never touched)
+  constexpr int SZA = DL ? 1 : 2 * BM * BK, SZB = DL ? 1 : 2 * BN * BK;
+  constexpr int RA = DL ? BM * BK : 1, RB = DL ? BN * BK : 1;
+  __shared__ __attribute__((aligned(16))) int8_t sA_[SZA];
+  __shared__ __attribute__((aligned(16))) int8_t sB_[SZB];
+  __shared__ __attribute__((aligned(16))) int8_t dA0[RA], dA1[RA], dA2[DL >= 3 ? RA : 1], dA3[DL >= 4 ? RA : 1];
+  __shared__ __attribute__((aligned(16))) int8_t dB0[RB], dB1[RB], dB2[DL >= 3 ? RB : 1], dB3[DL >= 4 ? RB : 1];
+  int8_t (*sA)[BM * BK] = reinterpret_cast<int8_t (*)[BM * BK]>(sA_);
+  int8_t (*sB)[BN * BK] = reinterpret_cast<int8_t (*)[BN * BK]>(sB_);
+  // the epilogue stages the outlier columns in the first buffer
+  int8_t* const ep_a = DL ? dA0 : sA_;
+  int8_t* const ep_b = DL ? dB0 : sB_;
 
   const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
   const int wm = wid / WGN, wn = wid % WGN;
   int tm, tn;
-  tile_coords<8>(blockIdx.x, tiles_m, tiles_n, tm, tn);
+  tile_coords<GM>(blockIdx.x, tiles_m, tiles_n, tm, tn);
   const int64_t m0 = (int64_t)tm * BM, n0 = (int64_t)tn * BN;
   const int n_idx = *n_idx_p;
 
@@ -216,31 +248,110 @@ __global__ __launch_bounds__(64 * WGM * WGN) void linear_tile_kernel(
     }
   };
 
-  gload(0, ra0, rb0);
-  gload(1, ra1, rb1);
-  fix_tail(0, ra0, rb0);
-  lstore(0, ra0, rb0);
-  __syncthreads();
-  read_frags(0, 0, fa0, fb0);
-  // Two steps per trip, no branch inside: on entry buffer 0 holds step kt
-  // (sub-step 0 operands in set 0) and register set 1 holds step kt + 1.
-  // Steps loaded or stored past the end are re-reads of the last one and are
-  // never multiplied.
-  int kt = 0;
-  for (; kt + 2 <= nk; kt += 2) {
-    step(0, kt, ra0, rb0, ra1, rb1);
-    step(1, kt + 1, ra1, rb1, ra0, rb0);
-  }
-  if (kt < nk) {  // odd step count: the last step sits in buffer 0
-#pragma unroll
-    for (int s = 0; s < SS; ++s) {
-      if (s + 1 < SS) {
-        if (s % 2 == 0) read_frags(0, s + 1, fa1, fb1);
-        else read_frags(0, s + 1, fa0, fb0);
-      }
-      if (s % 2 == 0) mfmas(fa0, fb0);
-      else mfmas(fa1, fb1);
+  if constexpr (DL == 0) {
+    gload(0, ra0, rb0);
+    gload(1, ra1, rb1);
+    fix_tail(0, ra0, rb0);
+    lstore(0, ra0, rb0);
+    __syncthreads();
+    read_frags(0, 0, fa0, fb0);
+    // Two steps per trip, no branch inside: on entry buffer 0 holds step kt
+    // (sub-step 0 operands in set 0) and register set 1 holds step kt + 1.
+    // Steps loaded or stored past the end are re-reads of the last one and are
+    // never multiplied.
+    int kt = 0;
+    for (; kt + 2 <= nk; kt += 2) {
+      step(0, kt, ra0, rb0, ra1, rb1);
+      step(1, kt + 1, ra1, rb1, ra0, rb0);
     }
+    if (kt < nk) {  // odd step count: the last step sits in buffer 0
+#pragma unroll
+      for (int s = 0; s < SS; ++s) {
+        if (s + 1 < SS) {
+          if (s % 2 == 0) read_frags(0, s + 1, fa1, fb1);
+          else read_frags(0, s + 1, fa0, fb0);
+        }
+        if (s % 2 == 0) mfmas(fa0, fb0);
+        else mfmas(fa1, fb1);
+      }
+    }
+  } else {
+    // Each load instruction moves RPI = 1024 / BK whole tile rows (1 KiB)
+    // straight into LDS, lane l to bytes 16 l .. 16 l + 15 of it.  The
+    // swizzle is applied on the source side: lane l of the instruction for
+    // rows r0 .. r0 + RPI - 1 fetches the logical chunk of row r = r0 + l / CPR
+    // that tile_off<BK> stores at physical chunk l % CPR.  No registers, no LDS
+    // store instructions; with 128-byte steps every row read is one whole
+    // cache line.  Every ring slot is an LDS object of its own
+    // and the loop is unrolled over the ring, so the compiler can tell the
+    // slot being read from the slots still being filled and waits only for
+    // the former.
+    constexpr int NW = WGM * WGN;
+    constexpr int RPI = 1024 / BK;                          // tile rows per load instruction
+    constexpr int IA = BM / RPI / NW, IB = BN / RPI / NW;  // load instructions per wave per step
+    static_assert(IA * RPI * NW == BM && IB * RPI * NW == BN, "tile rows must split evenly over the waves");
+    // logical chunk stored at physical chunk p of row r (the XOR is an involution)
+    auto src_chunk = [](int r, int p) { return BK == 64 ? (p ^ ((r >> 2) & 3)) : (p ^ ((r >> 1) & 7)); };
+    const int8_t* ga[IA];
+    const int8_t* gb[IB];
+#pragma unroll
+    for (int j = 0; j < IA; ++j) {
+      const int r = (wid * IA + j) * RPI + lane / CPR;
+      const int64_t row = m0 + r < T ? m0 + r : (int64_t)T - 1;
+      ga[j] = CA + row * K + (src_chunk(r, lane % CPR) << 4);
+    }
+#pragma unroll
+    for (int j = 0; j < IB; ++j) {
+      const int r = (wid * IB + j) * RPI + lane / CPR;
+      const int64_t row = n0 + r < N ? n0 + r : (int64_t)N - 1;
+      gb[j] = CB + row * K + (src_chunk(r, lane % CPR) << 4);
+    }
+    // step kt into ring slot st; steps past the end re-read the last one
+    // (never multiplied) so every wave issues the same number of loads
+    auto issue = [&](int kt, int8_t* a_slot, int8_t* b_slot) {
+      const int k = (kt < nk ? kt : nk - 1) * BK;
+#pragma unroll
+      for (int j = 0; j < IA; ++j) load_lds16(ga[j] + k, a_slot + (wid * IA + j) * 1024);
+#pragma unroll
+      for (int j = 0; j < IB; ++j) load_lds16(gb[j] + k, b_slot + (wid * IB + j) * 1024);
+    };
+    auto frags = [&](const int8_t* a_slot, const int8_t* b_slot, int s, v4i (&fa)[FM], v4i (&fb)[FN]) {
+      const int c = 2 * s + (lane >> 5);
+#pragma unroll
+      for (int i = 0; i < FM; ++i)
+        fa[i] = *reinterpret_cast<const v4i*>(a_slot + tile_off<BK>(wm * WM + i * 32 + (lane & 31), c));
+#pragma unroll
+      for (int j = 0; j < FN; ++j)
+        fb[j] = *reinterpret_cast<const v4i*>(b_slot + tile_off<BK>(wn * WN + j * 32 + (lane & 31), c));
+    };
+    int8_t* const ra[4] = {dA0, dA1, dA2, dA3};
+    int8_t* const rb[4] = {dB0, dB1, dB2, dB3};
+#pragma unroll
+    for (int st = 0; st < DL - 1; ++st) issue(st, ra[st], rb[st]);
+    for (int kg = 0; kg < nk; kg += DL) {
+#pragma unroll
+      for (int i = 0; i < DL; ++i) {
+        // all of step kg + i has landed once every wave is past the barrier,
+        // and everyone has finished reading slot i - 1 (one step ago)
+        wait_vmcnt<(DL - 2) * (IA + IB)>();
+        __builtin_amdgcn_s_barrier();
+        __builtin_amdgcn_sched_barrier(0);
+        issue(kg + i + DL - 1, ra[(i + DL - 1) % DL], rb[(i + DL - 1) % DL]);
+        if (kg + i < nk) {
+          frags(ra[i], rb[i], 0, fa0, fb0);
+#pragma unroll
+          for (int s2 = 0; s2 < SS; s2 += 2) {  // read sub-step s2 + 1 while s2 multiplies, and so on
+            frags(ra[i], rb[i], s2 + 1, fa1, fb1);
+            mfmas(fa0, fb0);
+            if (s2 + 2 < SS) frags(ra[i], rb[i], s2 + 2, fa0, fb0);
+            mfmas(fa1, fb1);
+          }
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+    wait_vmcnt<0>();  // the ring's last loads land before the epilogue reuses LDS
+    __syncthreads();
   }
 
   // ---- epilogue.  32x32 accumulator layout: lane holds column (lane & 31),
@@ -285,8 +396,8 @@ __global__ __launch_bounds__(64 * WGM * WGN) void linear_tile_kernel(
 
   // 16-bit outlier product, 32 outlier columns per step, LDS reused.
   const int n_chunks = (n_idx + 31) >> 5;
-  int8_t* oA = &sA[0][0];  // [BM][32] 16-bit values, 64-byte rows
-  int8_t* oB = &sB[0][0];  // [BN][32]
+  int8_t* oA = ep_a;  // [BM][32] 16-bit values, 64-byte rows
+  int8_t* oB = ep_b;  // [BN][32]
   for (int ch = 0; ch < n_chunks; ++ch) {
     __syncthreads();
 #pragma unroll
@@ -416,13 +527,19 @@ __global__ __launch_bounds__(256) void linear_decode_kernel(
   }
 }
 
-template <int DT, int BM, int BN, int BK, int WGM, int WGN>
+template <int DT, int BM, int BN, int BK, int WGM, int WGN, int GM = 8, int DL = 0>
 static hipError_t launch_tile(const LinearArgs& a, hipStream_t s) {
   const int tiles_m = (int)((a.T + BM - 1) / BM), tiles_n = (int)((a.N + BN - 1) / BN);
   const int nb = tiles_m * tiles_n;
-  auto k = (a.K % BK) == 0 ? linear_tile_kernel<DT, BM, BN, 0, BK, WGM, WGN>
-           : (a.K % 16) == 0 ? linear_tile_kernel<DT, BM, BN, 1, BK, WGM, WGN>
-                             : linear_tile_kernel<DT, BM, BN, 2, BK, WGM, WGN>;
+  decltype(&linear_tile_kernel<DT, BM, BN, 0, BK, WGM, WGN, GM, DL>) k;
+  if constexpr (DL != 0) {  // direct-load configurations need K a multiple of the step
+    if ((a.K % BK) != 0) return hipErrorInvalidValue;
+    k = linear_tile_kernel<DT, BM, BN, 0, BK, WGM, WGN, GM, DL>;
+  } else {
+    k = (a.K % BK) == 0 ? linear_tile_kernel<DT, BM, BN, 0, BK, WGM, WGN, GM, 0>
+        : (a.K % 16) == 0 ? linear_tile_kernel<DT, BM, BN, 1, BK, WGM, WGN, GM, 0>
+                          : linear_tile_kernel<DT, BM, BN, 2, BK, WGM, WGN, GM, 0>;
+  }
   k<<<dim3(nb), dim3(64 * WGM * WGN), 0, s>>>(a.CA, a.CB, a.SCA, a.SCB, static_cast<const uint16_t*>(a.bias),
                                    static_cast<const uint16_t*>(a.xo), a.idx, a.n_idx,
                                    static_cast<uint16_t*>(a.out), a.acc, (int)a.T, (int)a.N, (int)a.K,
@@ -439,7 +556,13 @@ static hipError_t launch_linear_t(const LinearArgs& a, hipStream_t s) {
         a.idx, a.n_idx, static_cast<uint16_t*>(a.out), a.acc, (int)a.T, (int)a.N, (int)a.K);
     return hipGetLastError();
   }
-  if (a.T >= 512 && a.N >= 512) return launch_tile<DT, 256, 256, 64, 4, 2>(a, s);
+  if (a.T >= 512 && a.N >= 512) {
+    // direct loads: 128-byte steps in a 2-slot ring (whole cache lines per
+    // row), else 64-byte steps in a 4-slot ring, else register staging
+    if (a.K % 128 == 0) return launch_tile<DT, 256, 256, 128, 4, 2, 4, 2>(a, s);
+    if (a.K % 64 == 0) return launch_tile<DT, 256, 256, 64, 4, 2, 4, 4>(a, s);
+    return launch_tile<DT, 256, 256, 64, 4, 2, 4, 0>(a, s);
+  }
   return launch_tile<DT, 128, 128, 64, 2, 2>(a, s);
 }
 
