@@ -37,57 +37,6 @@ constexpr int FD_MAXW = FD_MAXK / 32;         // bitmap words
 constexpr int FD_MPL = FD_MAXK / FD_LW / 64;  // MFMAs (64 columns each) per weight wave: 16
 constexpr int FD_OUT_LDS = 64;                // outlier columns staged in LDS; more read global memory
 
-// Codes of the two 16-bit values of x for row factor s = fl32(127 / absmax),
-// as two int16 in one dword.  v = fl32(|x| * s) <= 127.5 (for fp16 one
-// v_fma_mix_f32 with a zero addend: the same single rounding of the exact
-// product), and round-half-away(v) = floor(v + 0.5) for v >= 0, which
-// v_cvt_rpi_i32_f32 computes.  Its result is the same whether or not the
-// hardware rounds v + 0.5 to fp32 first: the one value where that rounding
-// would reach the next integer, v = 0.5 - 2^-25, is not the product of any
-// fp16 or bf16 value with the scale of any fp16 or bf16 absmax.  The sign of
-// x is applied to both magnitudes at once with packed 16-bit arithmetic.
-typedef short i16x2 __attribute__((ext_vector_type(2)));
-typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
-
-__device__ __forceinline__ int cvt_rpi(float v) {
-  int r;
-  asm("v_cvt_rpi_i32_f32 %0, %1" : "=v"(r) : "v"(v));
-  return r;
-}
-
-template <int DT>
-__device__ __forceinline__ float scaled_abs(uint32_t bits16, float s) {
-  if constexpr (DT == DT_F16)
-    return __builtin_fmaf(__builtin_fabsf((float)__builtin_bit_cast(_Float16, (uint16_t)bits16)), s, 0.0f);
-  else
-    return __uint_as_float((bits16 & 0x7FFFu) << 16) * s;
-}
-
-template <int DT>
-__device__ __forceinline__ uint32_t code_pair16(uint32_t x, float s) {
-  const int mlo = cvt_rpi(scaled_abs<DT>(x & 0xFFFFu, s));
-  const int mhi = cvt_rpi(scaled_abs<DT>(x >> 16, s));
-  const i16x2 mag = __builtin_bit_cast(i16x2, (uint32_t)mlo | ((uint32_t)mhi << 16));
-  const i16x2 neg = __builtin_bit_cast(i16x2, x) >> 15;  // -1 where x < 0
-  return __builtin_bit_cast(uint32_t, (i16x2)((mag ^ neg) - neg));
-}
-
-// Low bytes of the four int16 codes in two dwords, packed little-endian.
-__device__ __forceinline__ uint32_t pack_codes16(uint32_t p01, uint32_t p23) {
-  return __builtin_amdgcn_perm(p23, p01, 0x06040200u);
-}
-
-// Larger of each 16-bit half (v_pk_max_u16).
-__device__ __forceinline__ uint32_t pk_max_u16(uint32_t a, uint32_t b) {
-  return __builtin_bit_cast(uint32_t, __builtin_elementwise_max(__builtin_bit_cast(u16x2, a), __builtin_bit_cast(u16x2, b)));
-}
-
-// 0xFF in every byte whose bit is set in the low 4 bits of f.
-__device__ __forceinline__ uint32_t byte_mask4(uint32_t f) {
-  return ((f & 1u) * 0xFFu) | (((f >> 1) & 1u) * 0xFF00u) | (((f >> 2) & 1u) * 0xFF0000u) |
-         (((f >> 3) & 1u) * 0xFF000000u);
-}
-
 // Cross-lane moves without LDS: DPP within a row of 16 lanes, the gfx950
 // permlane swaps across rows.
 template <int CTRL>
@@ -188,14 +137,7 @@ __global__ __launch_bounds__(FD_THREADS, 1) void decode_fused_kernel(
   // (partial tiles) and B4 (epilogue done).
   if (w < FD_CW) {
     // ------------------------------------------------ activation waves ----
-    // |x| > tau  <=>  (bits & 0x7FFF) > t16, t16 = largest 16-bit magnitude <= tau
-    const bool outl = tau > 0.0f && tau <= 3.4028235e38f;
-    uint32_t t16 = 0xFFFFu;
-    if (outl) {
-      uint32_t bb = from_f32<DT>(tau);
-      if (to_f32<DT>(bb) > tau) bb -= 1u;
-      t16 = bb & 0x7FFFu;
-    }
+    const uint32_t t16 = magnitude_threshold<DT>(tau);  // |x| > tau  <=>  (bits & 0x7FFF) > t16
     // 1. chunk c = tid, columns 8c .. 8c + 7, all 16 rows.  Loads are
     // unconditional at clamped in-range addresses, so the compiler counts them
     // in order.  Rows beyond T repeat row T - 1 (harmless: they change no
@@ -228,11 +170,7 @@ __global__ __launch_bounds__(FD_THREADS, 1) void decode_fused_kernel(
       }
       rm[t] = pk_max_u16(pk_max_u16(a[0], a[1]), pk_max_u16(a[2], a[3]));
     }
-    uint32_t f8 = 0u;  // bit e: column 8c + e is an outlier column
-#pragma unroll
-    for (int d = 0; d < 4; ++d)
-      f8 |= (((cm[d] & 0xFFFFu) > t16) ? (1u << (2 * d)) : 0u) | (((cm[d] >> 16) > t16) ? (2u << (2 * d)) : 0u);
-    f8 = cok ? f8 : 0u;
+    const uint32_t f8 = cok ? flags8(cm, t16) : 0u;  // bit e: column 8c + e is an outlier column
     {  // bitmap word c / 4 from the four lanes of a quad; no atomics
       uint32_t wv = f8 << (8 * (c & 3));
       wv |= dpp<DPP_QUAD_XOR1>(wv);

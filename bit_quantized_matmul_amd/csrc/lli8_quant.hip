@@ -28,30 +28,37 @@ hipError_t launch_fill_u32(uint32_t* p, int64_t n, uint32_t v, hipStream_t s) {
 
 // --------------------------------------------------------- outlier scan ----
 // Column c is an outlier when some row has |X[t, c]| > tau.  Lane owns one
-// 16-byte chunk (8 columns) and walks rows; four lanes make one bitmap word,
+// 16-byte chunk (8 columns) and walks rows keeping packed 16-bit maxima of
+// the 15-bit magnitudes (one max per two values per row); the threshold test
+// is done once at the end on the raw bits.  Four lanes make one bitmap word,
 // which is OR-ed into the global bitmap only when non-zero (outlier columns
 // are rare, so atomics are rare).  Requires K % 8 == 0.
 template <int DT>
 __global__ __launch_bounds__(256) void scan_outliers_vec_kernel(
     const uint16_t* __restrict__ X, int64_t T, int64_t K, float tau,
     uint32_t* __restrict__ bitmap, int rows_per_block) {
+  constexpr int RPT = 8;  // rows per thread, loaded together
   const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
   const int64_t nch = K >> 3;
   const int64_t c = (int64_t)blockIdx.x * 64 + lane;
-  const int64_t r0 = (int64_t)blockIdx.y * rows_per_block;
-  const int64_t r1 = min(T, r0 + rows_per_block);
-  uint32_t flags = 0;
-  if (c < nch) {
-    const u32x4* p = reinterpret_cast<const u32x4*>(X) + c;
-    const int64_t stride = nch;  // chunks per row
-#pragma unroll 8
-    for (int64_t r = r0 + wid; r < r1; r += 4) {
-      const u32x4 v = p[r * stride];  // cached: the quantiser reads X again
+  const int64_t cc = c < nch ? c : nch - 1;
+  const u32x4* p = reinterpret_cast<const u32x4*>(X) + cc;
+  uint32_t m[4] = {0u, 0u, 0u, 0u};
+  for (int64_t rb = (int64_t)blockIdx.y * rows_per_block; rb < min(T, (int64_t)(blockIdx.y + 1) * rows_per_block);
+       rb += 4 * RPT) {
+    // rows past the end repeat the last row: a repeated row changes no maximum
+    u32x4 v[RPT];
 #pragma unroll
-      for (int e = 0; e < 8; ++e)
-        flags |= (fabsf(to_f32<DT>(half_bits(v, e))) > tau ? 1u : 0u) << e;
+    for (int i = 0; i < RPT; ++i) {
+      const int64_t r = rb + wid + 4 * i;
+      v[i] = p[(r < T ? r : T - 1) * nch];  // cached: the quantiser reads X again
     }
+#pragma unroll
+    for (int i = 0; i < RPT; ++i)
+#pragma unroll
+      for (int d = 0; d < 4; ++d) m[d] = pk_max_u16(m[d], v[i][d] & 0x7FFF7FFFu);
   }
+  const uint32_t flags = (c < nch) ? flags8(m, magnitude_threshold<DT>(tau)) : 0u;
   uint32_t w = flags << ((lane & 3) * 8);
   w |= __shfl_xor(w, 1, WAVE);
   w |= __shfl_xor(w, 2, WAVE);
@@ -85,9 +92,10 @@ hipError_t launch_scan_outliers(int dt, const void* X, int64_t T, int64_t K, flo
   const uint16_t* x = static_cast<const uint16_t*>(X);
   if ((K & 7) == 0) {
     const int64_t gx = (K / 8 + 63) / 64;
-    // Aim for >= ~2048 workgroups on big inputs, at most 64 rows per workgroup.
-    int rows = 64;
-    while (rows > 4 && gx * ((T + rows - 1) / rows) < 2048) rows >>= 1;
+    // 32 rows per pass of a workgroup (4 waves x 8 rows); passes per
+    // workgroup grow until the grid is about 1024 workgroups.
+    int rows = 32;
+    while (gx * ((T + 2 * rows - 1) / (2 * rows)) >= 1024 && rows < 1024) rows *= 2;
     const int64_t gy = (T + rows - 1) / rows;
     dim3 grid((unsigned)gx, (unsigned)gy);
     if (dt == DT_F16)
@@ -160,6 +168,10 @@ __device__ __forceinline__ void xo_zero_pad(uint16_t* __restrict__ xo, int total
 // One wave per row; the row stays in registers (MAXC 16-byte chunks per lane),
 // so HBM sees it once.  Requires K % 8 == 0 and K <= 512 * MAXC.
 // EXCL: activation mode (outlier columns excluded, index list, gather).
+// Row absmax as a packed 16-bit max of the 15-bit magnitudes (exact: the
+// largest bit pattern is the largest value); codes two at a time with
+// code_pair16.  Loads are unconditional at in-range addresses (chunks past
+// the row end re-read chunk 0 and are masked), so they are counted in order.
 template <int DT, bool EXCL, int MAXC>
 __global__ __launch_bounds__(256) void quant_rows_reg_kernel(
     const uint16_t* __restrict__ src, int64_t R, int64_t K, int8_t* __restrict__ codes,
@@ -181,53 +193,47 @@ __global__ __launch_bounds__(256) void quant_rows_reg_kernel(
 #pragma unroll
   for (int i = 0; i < MAXC; ++i) {
     const int64_t c = lane + (int64_t)i * WAVE;
-    if (c < nch) v[i] = __builtin_nontemporal_load(rp + c);
+    v[i] = __builtin_nontemporal_load(rp + (c < nch ? c : 0));
   }
-  float m = 0.0f;
+  uint32_t ob[MAXC];  // outlier columns of each chunk (bit e); chunks past the row end count as all-outlier
 #pragma unroll
   for (int i = 0; i < MAXC; ++i) {
     const int64_t c = lane + (int64_t)i * WAVE;
-    if (c < nch) {
-      uint32_t out_bits = 0;
-      if constexpr (EXCL) out_bits = (words[c >> 2] >> ((c & 3) * 8)) & 0xFFu;
-#pragma unroll
-      for (int e = 0; e < 8; ++e)
-        if (!((out_bits >> e) & 1u)) m = fmaxf(m, fabsf(to_f32<DT>(half_bits(v[i], e))));
-    }
+    uint32_t o = 0u;
+    if constexpr (EXCL) o = (words[c < nch ? (c >> 2) : 0] >> ((c & 3) * 8)) & 0xFFu;
+    ob[i] = (c < nch) ? o : 0xFFu;
   }
-  m = wave_max(m);
+  uint32_t mx = 0u;
+#pragma unroll
+  for (int i = 0; i < MAXC; ++i)
+#pragma unroll
+    for (int d = 0; d < 4; ++d) {
+      const uint32_t keep = (((ob[i] >> (2 * d)) & 1u) ? 0u : 0x7FFFu) | (((ob[i] >> (2 * d + 1)) & 1u) ? 0u : 0x7FFF0000u);
+      mx = pk_max_u16(mx, v[i][d] & keep);
+    }
+  mx = max(mx & 0xFFFFu, mx >> 16);
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) mx = max(mx, (uint32_t)__shfl_xor((int)mx, off, WAVE));
+  const float m = to_f32<DT>(mx);  // exact absmax of the kept values
   const float s = (m > 0.0f) ? 127.0f / m : 0.0f;
   u32x2* cp = reinterpret_cast<u32x2*>(codes + row * K);
 #pragma unroll
   for (int i = 0; i < MAXC; ++i) {
     const int64_t c = lane + (int64_t)i * WAVE;
-    if (c < nch) {
-      uint32_t out_bits = 0;
-      if constexpr (EXCL) out_bits = (words[c >> 2] >> ((c & 3) * 8)) & 0xFFu;
-      uint32_t lo = 0, hi = 0;
+    u32x2 pk;
+    pk[0] = pack_codes16(code_pair16<DT>(v[i][0], s), code_pair16<DT>(v[i][1], s)) & ~byte_mask4(ob[i]);
+    pk[1] = pack_codes16(code_pair16<DT>(v[i][2], s), code_pair16<DT>(v[i][3], s)) & ~byte_mask4(ob[i] >> 4);
+    if (c < nch) cp[c] = pk;
+    if constexpr (EXCL) {
+      if (c < nch && ob[i] && xo != nullptr) {
+        const uint32_t word = words[c >> 2];
+        const int base = (int)prefix[c >> 2];
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const uint32_t h = half_bits(v[i], e);
-        int q = 0;
-        if (!((out_bits >> e) & 1u) && m > 0.0f) q = quant_code(to_f32<DT>(h), s);
-        const uint32_t b = (uint32_t)(q & 0xFF);
-        if (e < 4) lo |= b << (8 * e); else hi |= b << (8 * (e - 4));
-      }
-      u32x2 pk;
-      pk[0] = lo;
-      pk[1] = hi;
-      cp[c] = pk;
-      if constexpr (EXCL) {
-        if (out_bits && xo != nullptr) {
-          const uint32_t word = words[c >> 2];
-          const int base = (int)prefix[c >> 2];
-#pragma unroll
-          for (int e = 0; e < 8; ++e) {
-            if ((out_bits >> e) & 1u) {
-              const int bit = (int)((c & 3) * 8 + e);
-              const int p = base + __popc(word & ((1u << bit) - 1u));
-              xo[xo_offset(p, row, R)] = (uint16_t)half_bits(v[i], e);
-            }
+        for (int e = 0; e < 8; ++e) {
+          if ((ob[i] >> e) & 1u) {
+            const int bit = (int)((c & 3) * 8 + e);
+            const int p = base + __popc(word & ((1u << bit) - 1u));
+            xo[xo_offset(p, row, R)] = (uint16_t)half_bits(v[i], e);
           }
         }
       }
