@@ -75,6 +75,8 @@ def lib() -> ctypes.CDLL:
     L.lli8_int8_linear.restype = i32
     L.lli8_scratch_bytes.argtypes = [i64, i64, i32]
     L.lli8_scratch_bytes.restype = ctypes.c_size_t
+    L.lli8_scratch_bytes_full.argtypes = [i64, i64, i64, i32]
+    L.lli8_scratch_bytes_full.restype = ctypes.c_size_t
     L.lli8_status_string.argtypes = [i32]
     L.lli8_status_string.restype = ctypes.c_char_p
     L.lli8_last_error.argtypes = []
@@ -104,6 +106,10 @@ def lli8_status_string(status: int) -> str:
 
 def lli8_scratch_bytes(T: int, K: int, dtype: int = LLI8_F16) -> int:
     return int(lib().lli8_scratch_bytes(T, K, dtype))
+
+
+def lli8_scratch_bytes_full(T: int, K: int, N: int, dtype: int = LLI8_F16) -> int:
+    return int(lib().lli8_scratch_bytes_full(T, K, N, dtype))
 
 
 # ------------------------------------------------------------ torch glue ----
@@ -170,7 +176,11 @@ def lli8_quant_rowwise_outliers(X, threshold: float, CA=None, SCA=None, bitmap=N
 class Workspace:
     """Caller-owned buffers of one forward call (torch tensors on one device)."""
 
-    def __init__(self, T: int, K: int, N: int, dtype, device, want_acc: bool = False):
+    def __init__(self, T: int, K: int, N: int, dtype, device, want_acc: bool = False,
+                 scratch_bytes: Optional[int] = None):
+        """scratch_bytes: None gives room for the recovered weights of every
+        possible outlier column (lli8_scratch_bytes_full); a smaller size is used
+        as far as it goes (at least lli8_scratch_bytes)."""
         torch = _torch()
         self.T, self.K, self.N = T, K, N
         self.CA = torch.empty((T, K), dtype=torch.int8, device=device)
@@ -179,7 +189,7 @@ class Workspace:
         self.idx = torch.empty((K,), dtype=torch.int32, device=device)
         self.n_idx = torch.zeros((1,), dtype=torch.int32, device=device)
         self.acc = torch.empty((T, N), dtype=torch.int32, device=device) if want_acc else None
-        nbytes = lli8_scratch_bytes(T, K, LLI8_F16)
+        nbytes = lli8_scratch_bytes_full(T, K, N, LLI8_F16) if scratch_bytes is None else int(scratch_bytes)
         self.scratch = torch.empty((max(nbytes, 16),), dtype=torch.uint8, device=device)
         self._struct = _Workspace(self.CA.data_ptr(), self.SCA.data_ptr(), self.bitmap.data_ptr(),
                                   self.idx.data_ptr(), self.n_idx.data_ptr(),

@@ -114,13 +114,21 @@ bool outliers_enabled(float tau) { return tau > 0.0f && isfinite(tau); }
 
 lli8_status_t enqueue_activation_split(const void* X, int64_t T, int64_t K, int dt, float tau, int8_t* CA,
                                        float* SCA, uint32_t* bitmap, int32_t* idx, int32_t* n_idx, void* xo,
+                                       const int8_t* CB, const float* SCB, int64_t N, void* wo, int wo_chunks,
                                        hipStream_t s) {
   const int64_t W = (K + 31) / 32;
   TRACED(s, "bitmap_clear", lli8::launch_fill_u32(bitmap, W, 0u, s));
   if (outliers_enabled(tau)) TRACED(s, "outlier_scan", lli8::launch_scan_outliers(dt, X, T, K, tau, bitmap, s));
   TRACED(s, "quant_activations", lli8::launch_quant_act(dt, X, T, K, bitmap, CA, SCA, idx, n_idx, xo, s));
+  if (wo != nullptr)
+    TRACED(s, "recover_outliers", lli8::launch_recover_outliers(dt, CB, SCB, N, K, idx, n_idx, wo, wo_chunks, s));
   return LLI8_OK;
 }
+
+// Scratch layout of lli8_int8_linear: gathered outlier columns of X
+// [ceil(K/32)][T][32], then, in whatever room is left, recovered outlier
+// weights [chunks][N][32] (16-bit each).
+size_t xo_bytes(int64_t T, int64_t K) { return (size_t)(T * ((K + 31) / 32 * 32) * 2); }
 
 }  // namespace
 
@@ -165,8 +173,12 @@ const char* lli8_status_string(lli8_status_t s) {
 size_t lli8_scratch_bytes(int64_t T, int64_t K, lli8_dtype_t dtype) {
   (void)dtype;  // both dtypes are 16-bit
   if (T <= 0 || K <= 0) return 0;
-  const int64_t kpad = (K + 31) / 32 * 32;
-  return (size_t)(T * kpad * 2);
+  return xo_bytes(T, K);
+}
+
+size_t lli8_scratch_bytes_full(int64_t T, int64_t K, int64_t N, lli8_dtype_t dtype) {
+  if (T <= 0 || K <= 0 || N <= 0) return lli8_scratch_bytes(T, K, dtype);
+  return xo_bytes(T, K) + (size_t)(N * ((K + 31) / 32 * 32) * 2);
 }
 
 lli8_status_t lli8_quant_weight_rowwise(const void* W, int64_t N, int64_t K, lli8_dtype_t dtype, int8_t* CB,
@@ -198,7 +210,8 @@ lli8_status_t lli8_quant_rowwise_outliers(const void* X, int64_t T, int64_t K, l
   REQUIRE(idx, "idx");
   REQUIRE(n_idx, "n_idx");
   hipStream_t s = static_cast<hipStream_t>(stream);
-  return enqueue_activation_split(X, T, K, (int)dtype, threshold, CA, SCA, bitmap, idx, n_idx, nullptr, s);
+  return enqueue_activation_split(X, T, K, (int)dtype, threshold, CA, SCA, bitmap, idx, n_idx, nullptr, nullptr,
+                                  nullptr, 0, nullptr, 0, s);
 }
 
 lli8_status_t lli8_int8_linear(const void* X, int64_t T, int64_t K, int64_t N, lli8_dtype_t dtype, const int8_t* CB,
@@ -250,8 +263,18 @@ lli8_status_t lli8_int8_linear(const void* X, int64_t T, int64_t K, int64_t N, l
     TRACED(s, "decode_fused", lli8::launch_decode_fused(f, s));
     return LLI8_OK;
   }
+  // room for recovered outlier weights after the gathered columns (tile path only)
+  void* wo = nullptr;
+  int wo_chunks = 0;
+  if (outl && T > 16) {
+    const size_t xb = xo_bytes(T, K), per_chunk = (size_t)N * 64;
+    const size_t room = ws->scratch_bytes > xb ? ws->scratch_bytes - xb : 0;
+    const int64_t c = (int64_t)(room / per_chunk), cmax = (K + 31) / 32;
+    wo_chunks = (int)(c < cmax ? c : cmax);
+    if (wo_chunks > 0) wo = static_cast<char*>(ws->scratch) + xb;
+  }
   TRY(enqueue_activation_split(X, T, K, (int)dtype, threshold, ws->CA, ws->SCA, ws->bitmap, ws->idx, ws->n_idx,
-                               outl ? ws->scratch : nullptr, s));
+                               outl ? ws->scratch : nullptr, CB, SCB, N, wo, wo_chunks, s));
   lli8::LinearArgs a;
   a.dt = (int)dtype;
   a.CA = ws->CA;
@@ -260,6 +283,8 @@ lli8_status_t lli8_int8_linear(const void* X, int64_t T, int64_t K, int64_t N, l
   a.SCB = SCB;
   a.bias = bias;
   a.xo = outl ? ws->scratch : nullptr;
+  a.wo = wo;
+  a.wo_chunks = wo_chunks;
   a.idx = ws->idx;
   a.n_idx = ws->n_idx;
   a.out = out;

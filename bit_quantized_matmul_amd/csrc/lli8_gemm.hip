@@ -97,7 +97,8 @@ __global__ __launch_bounds__(64 * WGM * WGN) void linear_tile_kernel(
     const int8_t* __restrict__ CA, const int8_t* __restrict__ CB, const float* __restrict__ SCA,
     const float* __restrict__ SCB, const uint16_t* __restrict__ bias, const uint16_t* __restrict__ xo,
     const int32_t* __restrict__ idx, const int32_t* __restrict__ n_idx_p, uint16_t* __restrict__ out,
-    int32_t* __restrict__ acc_out, int T, int N, int K, int tiles_m, int tiles_n) {
+    int32_t* __restrict__ acc_out, int T, int N, int K, int tiles_m, int tiles_n,
+    const uint16_t* __restrict__ wo, int wo_chunks) {
   constexpr int NT = 64 * WGM * WGN;                    // threads: WGM x WGN waves
   constexpr int WM = BM / WGM, WN = BN / WGN;
   constexpr int FM = WM / 32, FN = WN / 32;
@@ -105,7 +106,7 @@ __global__ __launch_bounds__(64 * WGM * WGN) void linear_tile_kernel(
   constexpr int SS = BK / 32;                           // MFMA sub-steps per K step
   constexpr int LA = BM * CPR / NT, LB = BN * CPR / NT;  // 16-byte chunks per thread per step
   static_assert(LA * NT == BM * CPR && LB * NT == BN * CPR, "tile rows must split evenly over the threads");
-  static_assert(BK == 64 || (BM * 4) % NT == 0, "outlier staging reuses the 64-byte tile rows");
+  static_assert((BM * 4) % NT == 0 && (BN * 4) % NT == 0, "outlier staging: 64-byte rows split evenly over the threads");
   static_assert(DL == 0 || (DL >= 2 && DL <= 4 && KM == 0), "direct loads: K a multiple of the step");
   // register-staged loads: one double-buffered array each; direct loads: one
   // LDS object per ring slot (slots beyond DL are never touched)
@@ -248,7 +249,9 @@ __global__ __launch_bounds__(64 * WGM * WGN) void linear_tile_kernel(
     }
   };
 
-  if constexpr (DL == 0) {
+  if (n_idx >= K) {
+    // every column is an outlier column: CA is all zeros, nothing to multiply
+  } else if constexpr (DL == 0) {
     gload(0, ra0, rb0);
     gload(1, ra1, rb1);
     fix_tail(0, ra0, rb0);
@@ -407,7 +410,15 @@ __global__ __launch_bounds__(64 * WGM * WGN) void linear_tile_kernel(
       if (m0 + r < T) v = *reinterpret_cast<const u32x4*>(xo + (((int64_t)ch * T + m0 + r) * 32 + c * 8));
       *reinterpret_cast<u32x4*>(oA + lds_off(r, c)) = v;
     }
-    {
+    if (ch < wo_chunks) {  // recovered weights precomputed once per call: contiguous rows
+#pragma unroll
+      for (int i = 0; i < BN * 4 / NT; ++i) {
+        const int q = tid + NT * i, r = q >> 2, c = q & 3;
+        u32x4 v = {0u, 0u, 0u, 0u};
+        if (n0 + r < N) v = *reinterpret_cast<const u32x4*>(wo + (((int64_t)ch * N + n0 + r) * 32 + c * 8));
+        *reinterpret_cast<u32x4*>(oB + lds_off(r, c)) = v;
+      }
+    } else {  // gathered here
       const int j = tid & 31;
       const int p = ch * 32 + j;
       const bool valid = p < n_idx;
@@ -543,7 +554,7 @@ static hipError_t launch_tile(const LinearArgs& a, hipStream_t s) {
   k<<<dim3(nb), dim3(64 * WGM * WGN), 0, s>>>(a.CA, a.CB, a.SCA, a.SCB, static_cast<const uint16_t*>(a.bias),
                                    static_cast<const uint16_t*>(a.xo), a.idx, a.n_idx,
                                    static_cast<uint16_t*>(a.out), a.acc, (int)a.T, (int)a.N, (int)a.K,
-                                   tiles_m, tiles_n);
+                                   tiles_m, tiles_n, static_cast<const uint16_t*>(a.wo), a.wo ? a.wo_chunks : 0);
   return hipGetLastError();
 }
 

@@ -18,6 +18,11 @@ hipError_t launch_quant_act(int dt, const void* X, int64_t T, int64_t K, const u
                             int8_t* CA, float* SCA, int32_t* idx, int32_t* n_idx, void* xo,
                             hipStream_t s);
 
+// Recovered weights of the first min(ceil(n/32), chunks) outlier chunks,
+// chunk-major [chunk][N][32] 16-bit (n read on the device).
+hipError_t launch_recover_outliers(int dt, const int8_t* CB, const float* SCB, int64_t N, int64_t K,
+                                   const int32_t* idx, const int32_t* n_idx, void* wo, int chunks, hipStream_t s);
+
 struct LinearArgs {
   int dt;
   const int8_t* CA;
@@ -26,6 +31,8 @@ struct LinearArgs {
   const float* SCB;
   const void* bias;      // may be null
   const void* xo;        // gathered outlier columns, chunk-major [ceil(n/32)][T][32]
+  const void* wo;        // recovered weights of the first wo_chunks outlier chunks, [wo_chunks][N][32]
+  int wo_chunks;
   const int32_t* idx;
   const int32_t* n_idx;  // device
   void* out;

@@ -335,4 +335,51 @@ hipError_t launch_quant_act(int dt, const void* X, int64_t T, int64_t K, const u
   return launch_quant_rows_t<DT_BF16, true>(x, T, K, CA, SCA, bitmap, idx, n_idx, g, s);
 }
 
+// ------------------------------------------------ recovered outlier weights ----
+// dtype(fl32(fl32(CB * SCB) / 127)) ("Integration into transformers") of the
+// outlier columns, written once per call chunk-major [chunk][N][32] (zero
+// beyond n) so that every GEMM tile reads them as contiguous 64-byte rows
+// instead of gathering single bytes of CB.  Thread = one 16-byte piece (8
+// values) of one row; the columns come from the index list.  A fixed grid
+// walks however many chunks this call's n fills (at most `chunks`).
+template <int DT>
+__global__ __launch_bounds__(256) void recover_outliers_kernel(
+    const int8_t* __restrict__ CB, const float* __restrict__ SCB, int64_t N, int64_t K,
+    const int32_t* __restrict__ idx, const int32_t* __restrict__ n_idx_p, uint16_t* __restrict__ wo, int chunks) {
+  const int total = *n_idx_p;
+  const int used = min((total + 31) >> 5, chunks);
+  const int64_t per_row = (int64_t)used * 4;  // pieces per row
+  const int64_t pieces = per_row * N;
+  for (int64_t q = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; q < pieces; q += (int64_t)gridDim.x * blockDim.x) {
+    const int64_t n = q / per_row;
+    const int cp = (int)(q - n * per_row);  // chunk * 4 + part
+    const int p0 = cp * 8;
+    const float scb = SCB[n];
+    const int8_t* cbrow = CB + n * K;
+    uint32_t v[4] = {0u, 0u, 0u, 0u};
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      if (p0 + e < total) {
+        const uint32_t w = from_f32<DT>(((float)cbrow[idx[p0 + e]] * scb) / 127.0f);
+        v[e >> 1] |= w << (16 * (e & 1));
+      }
+    }
+    *reinterpret_cast<u32x4*>(wo + (((int64_t)(cp >> 2) * N + n) * 32 + (cp & 3) * 8)) = (u32x4){v[0], v[1], v[2], v[3]};
+  }
+}
+
+hipError_t launch_recover_outliers(int dt, const int8_t* CB, const float* SCB, int64_t N, int64_t K,
+                                   const int32_t* idx, const int32_t* n_idx, void* wo, int chunks, hipStream_t s) {
+  if (wo == nullptr || chunks <= 0 || N <= 0) return hipSuccess;
+  const int64_t most = (int64_t)chunks * 4 * N;  // pieces if every chunk is used
+  const int64_t want = (most + 255) / 256;
+  const int64_t blocks = want < 4096 ? want : 4096;
+  uint16_t* w = static_cast<uint16_t*>(wo);
+  if (dt == DT_F16)
+    recover_outliers_kernel<DT_F16><<<dim3((unsigned)blocks), 256, 0, s>>>(CB, SCB, N, K, idx, n_idx, w, chunks);
+  else
+    recover_outliers_kernel<DT_BF16><<<dim3((unsigned)blocks), 256, 0, s>>>(CB, SCB, N, K, idx, n_idx, w, chunks);
+  return hipGetLastError();
+}
+
 }  // namespace lli8

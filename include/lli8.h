@@ -120,8 +120,16 @@ typedef struct lli8_workspace {
   size_t scratch_bytes;
 } lli8_workspace_t;
 
-/* Bytes of scratch lli8_int8_linear needs for these sizes. */
+/* Bytes of scratch lli8_int8_linear needs for these sizes (the minimum:
+ * the gathered outlier columns of X). */
 size_t lli8_scratch_bytes(int64_t T, int64_t K, lli8_dtype_t dtype);
+
+/* Bytes of scratch that also hold the recovered weights (CB * SCB) / 127 of
+ * every possible outlier column for an N-row weight: with this much, each
+ * call recovers them once instead of in every output tile (the fast path
+ * when many columns are outliers).  Any size in between is used as far as it
+ * goes, in whole 32-column chunks of N * 64 bytes. */
+size_t lli8_scratch_bytes_full(int64_t T, int64_t K, int64_t N, lli8_dtype_t dtype);
 
 /*
  * The whole forward, "Core idea of LLM.int8()" steps 1-3:

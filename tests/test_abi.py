@@ -51,6 +51,8 @@ def test_scratch_bytes():
     assert L.lli8_scratch_bytes(8, 64) == 8 * 64 * 2
     assert L.lli8_scratch_bytes(8, 65) == 8 * 96 * 2
     assert L.lli8_scratch_bytes(4096, 12288, L.LLI8_BF16) == 4096 * 12288 * 2
+    assert L.lli8_scratch_bytes_full(8, 65, 10) == 8 * 96 * 2 + 10 * 96 * 2
+    assert L.lli8_scratch_bytes_full(0, 64, 10) == 0
 
 
 FAKE = 0x100000  # a 16-byte aligned non-null address; never dereferenced

@@ -210,3 +210,37 @@ def test_fused_decode_many_blocks_per_workgroup():
     """N well beyond one 16-feature block per CU: each workgroup walks several blocks."""
     case = random_case(7, 512, 16 * 256 * 3 + 5, seed=78, n_out=2)
     _check_full(case)
+
+
+@pytest.mark.parametrize("room_chunks", ["full", 0, 1])
+def test_recovered_outlier_weights_scratch_sizes(room_chunks):
+    """The recovered outlier weights come from scratch for as many 32-column
+    chunks as fit and are gathered in the tiles for the rest; every split
+    gives the oracle's results (here 70 outlier columns: three chunks)."""
+    B = _lib()
+    import torch
+    case = random_case(300, 512, 260, seed=31, n_out=70)
+    X = to_dev(case.X, case.dtype)
+    W = to_dev(case.W, case.dtype)
+    CB, SCB = B.lli8_quant_weight_rowwise(W)
+    if room_chunks == "full":
+        nbytes = None
+    else:
+        nbytes = B.lli8_scratch_bytes(case.T, case.K) + room_chunks * case.N * 64
+    ws = B.Workspace(case.T, case.K, case.N, X.dtype, X.device, want_acc=True, scratch_bytes=nbytes)
+    out, ws = B.lli8_int8_linear(X, CB, SCB, None, case.threshold, ws=ws, want_acc=True)
+    torch.cuda.synchronize()
+    rCB, rSCB = O.quantize_weight_bits(case.W, case.dtype)
+    r = O.linear_forward(case.X, case.dtype, rCB, rSCB, None, case.threshold)
+    assert int(ws.n_idx.item()) == r["idx"].size == 70
+    assert np.array_equal(ws.acc.cpu().numpy(), r["acc"])
+    assert normwise_rel(bits_of(out), r["out64"], case.dtype) <= OUT_TOL
+
+
+def test_every_column_an_outlier_skips_nothing_it_needs():
+    """All K columns flagged (tiny threshold): the int8 product is skipped and
+    the output is the 16-bit product alone."""
+    case = random_case(290, 256, 300, seed=33, n_out=0)
+    g, r = _check_full(case, 0.01)
+    assert g["n"] == case.K
+    assert not g["acc"].any()
