@@ -8,6 +8,8 @@ dequantisation, 16-bit outlier product and bias (and, for the workloads whose
 weights are quantised on every call, the weight quantisation before it).
 
 Timing protocol.  All inputs are resident in HBM before the timed region.
+Untimed steps run for --settle-ms (200 ms) so the clocks have left idle, then
+the W warm-up steps.
 They exist in R identical copies at different addresses (R chosen so that one
 pass over the copies moves >= 768 MiB, three times the 256 MB Infinity
 Cache), and step i uses copy i mod R -- the way consecutive layers of a model
@@ -49,6 +51,8 @@ def parse():
     p.add_argument("--rotate-mib", type=float, default=768.0,
                    help="input copies are rotated until one pass moves this many MiB")
     p.add_argument("--cpu-seconds", type=float, default=10.0, help="target CPU-oracle time")
+    p.add_argument("--settle-ms", type=float, default=200.0,
+                   help="untimed steps run for this long before the warm-up, so the clocks have settled")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--copy-mib", type=float, default=0.0,
                    help="instead of the benchmark, run 10 plain device-to-device copies of this "
@@ -209,6 +213,15 @@ def main():
             B.lli8_quant_weight_rowwise(cp["W"], cp["CB"], cp["SCB"])
         B.lli8_int8_linear(cp["X"], cp["CB"], cp["SCB"], cp["bias"], case.threshold, out=out, ws=ws)
 
+    # clocks: an idle GPU ramps up over tens of milliseconds; run untimed
+    # steps until they have settled, then the W warm-up steps
+    t_settle = time.perf_counter()
+    n_settle = 0
+    while (time.perf_counter() - t_settle) * 1e3 < args.settle_ms:
+        for _ in range(8):
+            step(n_settle)
+            n_settle += 1
+        torch.cuda.synchronize()
     for i in range(args.warmup):
         step(i)
     torch.cuda.synchronize()
@@ -267,6 +280,7 @@ def main():
                    "threshold": case.threshold, "n_idx": n_idx, "bias": case.bias is not None,
                    "weights": "quantised every call" if case.weights_each_call else "pre-quantised",
                    "input_copies_rotated": R, "rotation_mib": round(R * copy_bytes / 2 ** 20, 1),
+                   "settle_steps": n_settle,
                    "step_algorithmic_bytes": step_bytes(case),
                    "step_hbm_frac": round(step_bytes(case) / (ms * 1e-3) / (HBM_PEAK_GBS * 1e9), 4),
                    "kernels_ms": {k: round(v, 5) for k, v in avg.items()},

@@ -397,11 +397,79 @@ __global__ __launch_bounds__(64 * WGM * WGN) void linear_tile_kernel(
     __builtin_amdgcn_sched_barrier(0);  // keep the per-row loads of one strip at a time
   }
 
-  // 16-bit outlier product, 32 outlier columns per step, LDS reused.
+  // 16-bit outlier product, 32 outlier columns per step.
   const int n_chunks = (n_idx + 31) >> 5;
+  int ch_done = 0;
+  if constexpr (DL != 0) {
+    // With the recovered weights in scratch, both operands are chunk-major
+    // 64-byte rows: the chunks stream through the same LDS ring as the int8
+    // steps (direct loads, DL slots), into the dequantised fp32 registers.
+    if (n_chunks > 0 && n_chunks <= wo_chunks) {
+      constexpr int NW = WGM * WGN;
+      constexpr int IA = BM / 16 / NW, IB = BN / 16 / NW;  // 1 KiB loads per wave per chunk (16 rows each)
+      static_assert(IA * 16 * NW == BM && IB * 16 * NW == BN, "tile rows must split evenly over the waves");
+      const int8_t* xa[IA];
+      const int8_t* wb[IB];
+#pragma unroll
+      for (int j = 0; j < IA; ++j) {
+        const int r = (wid * IA + j) * 16 + (lane >> 2);
+        const int64_t row = m0 + r < T ? m0 + r : (int64_t)T - 1;
+        xa[j] = reinterpret_cast<const int8_t*>(xo) + row * 64 + (((lane & 3) ^ ((r >> 2) & 3)) << 4);
+      }
+#pragma unroll
+      for (int j = 0; j < IB; ++j) {
+        const int r = (wid * IB + j) * 16 + (lane >> 2);
+        const int64_t row = n0 + r < N ? n0 + r : (int64_t)N - 1;
+        wb[j] = reinterpret_cast<const int8_t*>(wo) + row * 64 + (((lane & 3) ^ ((r >> 2) & 3)) << 4);
+      }
+      auto issue16 = [&](int ch, int8_t* a_slot, int8_t* b_slot) {
+        const int c = ch < n_chunks ? ch : n_chunks - 1;
+        const int64_t oa = (int64_t)c * T * 64, ob = (int64_t)c * N * 64;
+#pragma unroll
+        for (int j = 0; j < IA; ++j) load_lds16(xa[j] + oa, a_slot + (wid * IA + j) * 1024);
+#pragma unroll
+        for (int j = 0; j < IB; ++j) load_lds16(wb[j] + ob, b_slot + (wid * IB + j) * 1024);
+      };
+      int8_t* const ra[4] = {dA0, dA1, dA2, dA3};
+      int8_t* const rb[4] = {dB0, dB1, dB2, dB3};
+      __syncthreads();  // everyone is done with the ring's int8 contents
+#pragma unroll
+      for (int st = 0; st < DL - 1; ++st) issue16(st, ra[st], rb[st]);
+      for (int cg = 0; cg < n_chunks; cg += DL) {
+#pragma unroll
+        for (int i = 0; i < DL; ++i) {
+          wait_vmcnt<(DL - 2) * (IA + IB)>();
+          __builtin_amdgcn_s_barrier();
+          __builtin_amdgcn_sched_barrier(0);
+          issue16(cg + i + DL - 1, ra[(i + DL - 1) % DL], rb[(i + DL - 1) % DL]);
+          if (cg + i < n_chunks) {
+#pragma unroll
+            for (int s2 = 0; s2 < 2; ++s2) {
+              const int c = 2 * s2 + (lane >> 5);
+              u32x4 a[FM], b[FN];
+#pragma unroll
+              for (int ii = 0; ii < FM; ++ii)
+                a[ii] = *reinterpret_cast<const u32x4*>(ra[i] + tile_off<64>(wm * WM + ii * 32 + (lane & 31), c));
+#pragma unroll
+              for (int jj = 0; jj < FN; ++jj)
+                b[jj] = *reinterpret_cast<const u32x4*>(rb[i] + tile_off<64>(wn * WN + jj * 32 + (lane & 31), c));
+#pragma unroll
+              for (int ii = 0; ii < FM; ++ii)
+#pragma unroll
+                for (int jj = 0; jj < FN; ++jj)
+                  acc[ii][jj] = __builtin_bit_cast(v16i, mfma16<DT>(a[ii], b[jj], __builtin_bit_cast(v16f, acc[ii][jj])));
+            }
+          }
+          __builtin_amdgcn_sched_barrier(0);
+        }
+      }
+      wait_vmcnt<0>();
+      ch_done = n_chunks;
+    }
+  }
   int8_t* oA = ep_a;  // [BM][32] 16-bit values, 64-byte rows
   int8_t* oB = ep_b;  // [BN][32]
-  for (int ch = 0; ch < n_chunks; ++ch) {
+  for (int ch = ch_done; ch < n_chunks; ++ch) {
     __syncthreads();
 #pragma unroll
     for (int i = 0; i < BM * 4 / NT; ++i) {

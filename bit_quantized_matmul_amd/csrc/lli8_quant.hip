@@ -357,11 +357,28 @@ __global__ __launch_bounds__(256) void recover_outliers_kernel(
     const float scb = SCB[n];
     const int8_t* cbrow = CB + n * K;
     uint32_t v[4] = {0u, 0u, 0u, 0u};
+    const int c0 = (p0 < total) ? idx[p0] : 0;
+    if (p0 + 8 <= total && (K & 3) == 0 && idx[p0 + 7] - c0 == 7) {
+      // eight consecutive columns (every column an outlier, say): three
+      // aligned dwords cover them
+      const int a0 = c0 & ~3, sh = c0 & 3;
+      const uint32_t* src = reinterpret_cast<const uint32_t*>(cbrow + a0);
+      const uint32_t d0 = src[0], d1 = src[1], d2 = (sh != 0) ? src[2] : 0u;
+      const uint32_t lo = (uint32_t)(((uint64_t)d1 << 32 | d0) >> (8 * sh));
+      const uint32_t hi = (uint32_t)(((uint64_t)d2 << 32 | d1) >> (8 * sh));
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      if (p0 + e < total) {
-        const uint32_t w = from_f32<DT>(((float)cbrow[idx[p0 + e]] * scb) / 127.0f);
+      for (int e = 0; e < 8; ++e) {
+        const int8_t cb = (int8_t)(((e < 4 ? lo : hi) >> (8 * (e & 3))) & 0xFFu);
+        const uint32_t w = from_f32<DT>(((float)cb * scb) / 127.0f);
         v[e >> 1] |= w << (16 * (e & 1));
+      }
+    } else {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        if (p0 + e < total) {
+          const uint32_t w = from_f32<DT>(((float)cbrow[idx[p0 + e]] * scb) / 127.0f);
+          v[e >> 1] |= w << (16 * (e & 1));
+        }
       }
     }
     *reinterpret_cast<u32x4*>(wo + (((int64_t)(cp >> 2) * N + n) * 32 + (cp & 3) * 8)) = (u32x4){v[0], v[1], v[2], v[3]};
