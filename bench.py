@@ -77,6 +77,8 @@ def kernel_bytes(name, case, n_idx):
         return 2 * T * K + N * K + 4 * N + bias + 2 * T * N
     if name == "bitmap_clear":
         return 4 * ((K + 31) // 32)
+    if name == "recover_outliers":  # CB at the outlier columns in, recovered rows out
+        return N * n_idx + 4 * N + 4 * n_idx + 2 * N * npad
     return 0
 
 
@@ -91,6 +93,7 @@ def step_bytes(case):
 KERNEL_SOURCES = {
     "int8_gemm": "lli8_gemm.hip", "decode_fused": "lli8_decode.hip", "quant_activations": "lli8_quant.hip",
     "outlier_scan": "lli8_quant.hip", "quant_weight": "lli8_quant.hip", "bitmap_clear": "lli8_quant.hip",
+    "recover_outliers": "lli8_quant.hip",
 }
 
 

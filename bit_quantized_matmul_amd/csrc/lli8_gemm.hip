@@ -89,6 +89,19 @@ __device__ __forceinline__ void load_lds16(const int8_t* g, int8_t* lds) {
   __builtin_amdgcn_global_load_lds(g, (__attribute__((address_space(3))) void*)lds, 16, 0, 0);
 }
 
+// Scheduling hint for the region since the last sched_barrier: its MFMAs,
+// LDS reads and global loads in round robin, one of each at a time, so that
+// the reads and loads issue while earlier MFMAs occupy the matrix core.
+template <int NM, int NR, int NL>
+__device__ __forceinline__ void interleave_mfma() {
+#pragma unroll
+  for (int m = 0; m < NM; ++m) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
+    if constexpr (NR > 0) if (m < NR) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // LDS read
+    if constexpr (NL > 0) if (m < NL) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);  // global load
+  }
+}
+
 // DL = 0: global loads staged through registers, LDS double buffered (any K).
 // DL = D >= 3 (K % 64 == 0 only): loads go straight from global memory into a
 // D-stage LDS ring, D - 1 steps ahead.
@@ -280,43 +293,50 @@ __global__ __launch_bounds__(64 * WGM * WGN) void linear_tile_kernel(
     }
   } else {
     // Each load instruction moves RPI = 1024 / BK whole tile rows (1 KiB)
-    // straight into LDS, lane l to bytes 16 l .. 16 l + 15 of it.  The
-    // swizzle is applied on the source side: lane l of the instruction for
-    // rows r0 .. r0 + RPI - 1 fetches the logical chunk of row r = r0 + l / CPR
-    // that tile_off<BK> stores at physical chunk l % CPR.  No registers, no LDS
-    // store instructions; with 128-byte steps every row read is one whole
-    // cache line.  Every ring slot is an LDS object of its own
-    // and the loop is unrolled over the ring, so the compiler can tell the
-    // slot being read from the slots still being filled and waits only for
-    // the former.
+    // straight into LDS (global_load_lds), lane l to bytes 16 l .. 16 l + 15
+    // of it.  The swizzle is applied on the source side: lane l of the
+    // instruction for rows r0 .. r0 + RPI - 1 fetches the logical chunk of row
+    // r = r0 + l / CPR that tile_off<BK> stores at physical chunk l % CPR.
+    // Rows past T or N re-read the last row (their results are never
+    // stored).  The tile's rows span less than 2^32 bytes (256 K-byte rows,
+    // K below 2^24), so 32-bit offsets reach them.  No registers, no LDS
+    // store instructions;
+    // with 128-byte steps every row read is one whole cache line.  Every ring
+    // slot is an LDS object of its own and the loop is unrolled over the ring,
+    // so the compiler can tell the slot being read from the slots still being
+    // filled and waits only for the former.
     constexpr int NW = WGM * WGN;
     constexpr int RPI = 1024 / BK;                          // tile rows per load instruction
     constexpr int IA = BM / RPI / NW, IB = BN / RPI / NW;  // load instructions per wave per step
     static_assert(IA * RPI * NW == BM && IB * RPI * NW == BN, "tile rows must split evenly over the waves");
     // logical chunk stored at physical chunk p of row r (the XOR is an involution)
     auto src_chunk = [](int r, int p) { return BK == 64 ? (p ^ ((r >> 2) & 3)) : (p ^ ((r >> 1) & 7)); };
-    const int8_t* ga[IA];
-    const int8_t* gb[IB];
+    // per-lane 32-bit offsets from the tile's first row; the wave-uniform
+    // base (this tile's rows, this step) goes in scalar registers
+    const int swid = __builtin_amdgcn_readfirstlane(wid);
+    uint32_t oa[IA], ob[IB];
 #pragma unroll
     for (int j = 0; j < IA; ++j) {
       const int r = (wid * IA + j) * RPI + lane / CPR;
-      const int64_t row = m0 + r < T ? m0 + r : (int64_t)T - 1;
-      ga[j] = CA + row * K + (src_chunk(r, lane % CPR) << 4);
+      const int rr = m0 + r < T ? r : (int)(T - 1 - m0);
+      oa[j] = (uint32_t)rr * (uint32_t)K + (uint32_t)(src_chunk(r, lane % CPR) << 4);
     }
 #pragma unroll
     for (int j = 0; j < IB; ++j) {
       const int r = (wid * IB + j) * RPI + lane / CPR;
-      const int64_t row = n0 + r < N ? n0 + r : (int64_t)N - 1;
-      gb[j] = CB + row * K + (src_chunk(r, lane % CPR) << 4);
+      const int rr = n0 + r < N ? r : (int)(N - 1 - n0);
+      ob[j] = (uint32_t)rr * (uint32_t)K + (uint32_t)(src_chunk(r, lane % CPR) << 4);
     }
-    // step kt into ring slot st; steps past the end re-read the last one
-    // (never multiplied) so every wave issues the same number of loads
+    const int8_t* const ta = CA + m0 * K;
+    const int8_t* const tb = CB + n0 * K;
+    // step kt into a ring slot; a step past the end (never multiplied)
+    // re-reads the last one, still in L2
     auto issue = [&](int kt, int8_t* a_slot, int8_t* b_slot) {
-      const int k = (kt < nk ? kt : nk - 1) * BK;
+      const int64_t k = (int64_t)(kt < nk ? kt : nk - 1) * BK;
 #pragma unroll
-      for (int j = 0; j < IA; ++j) load_lds16(ga[j] + k, a_slot + (wid * IA + j) * 1024);
+      for (int j = 0; j < IA; ++j) load_lds16(ta + k + oa[j], a_slot + (swid * IA + j) * 1024);
 #pragma unroll
-      for (int j = 0; j < IB; ++j) load_lds16(gb[j] + k, b_slot + (wid * IB + j) * 1024);
+      for (int j = 0; j < IB; ++j) load_lds16(tb + k + ob[j], b_slot + (swid * IB + j) * 1024);
     };
     auto frags = [&](const int8_t* a_slot, const int8_t* b_slot, int s, v4i (&fa)[FM], v4i (&fb)[FN]) {
       const int c = 2 * s + (lane >> 5);
@@ -329,28 +349,78 @@ __global__ __launch_bounds__(64 * WGM * WGN) void linear_tile_kernel(
     };
     int8_t* const ra[4] = {dA0, dA1, dA2, dA3};
     int8_t* const rb[4] = {dB0, dB1, dB2, dB3};
+    if constexpr (DL == 2) {
+      // Two slots, two steps in flight.  Sub-step s + 1's operands are read
+      // while sub-step s multiplies, one LDS read between consecutive MFMAs.
+      // The step's one barrier sits before its last sub-step's MFMAs: those
+      // keep the matrix cores busy across the barrier, the loads of step
+      // kt + 2 into the slot just released and the reads of step kt + 1's
+      // first operands.  Each wave waits for all its loads and LDS reads
+      // before the barrier, so once past it every load of step kt + 1 has
+      // landed and nobody reads slot kt any more.  Past the last step the
+      // loads are out of range and the reads are of a slot nobody uses.
+      constexpr int NFR = FM + FN;  // LDS reads per sub-step
+      constexpr int NLD = IA + IB;  // loads per step
+      static_assert(SS % 2 == 0, "operand sets alternate over an even number of sub-steps");
+      // one step out of slot `cur` (its sub-step 0 operands already in set 0)
+      auto kstep = [&](int kt, int8_t* a_cur, int8_t* b_cur, const int8_t* a_nxt, const int8_t* b_nxt) {
 #pragma unroll
-    for (int st = 0; st < DL - 1; ++st) issue(st, ra[st], rb[st]);
-    for (int kg = 0; kg < nk; kg += DL) {
-#pragma unroll
-      for (int i = 0; i < DL; ++i) {
-        // all of step kg + i has landed once every wave is past the barrier,
-        // and everyone has finished reading slot i - 1 (one step ago)
-        wait_vmcnt<(DL - 2) * (IA + IB)>();
-        __builtin_amdgcn_s_barrier();
-        __builtin_amdgcn_sched_barrier(0);
-        issue(kg + i + DL - 1, ra[(i + DL - 1) % DL], rb[(i + DL - 1) % DL]);
-        if (kg + i < nk) {
-          frags(ra[i], rb[i], 0, fa0, fb0);
-#pragma unroll
-          for (int s2 = 0; s2 < SS; s2 += 2) {  // read sub-step s2 + 1 while s2 multiplies, and so on
-            frags(ra[i], rb[i], s2 + 1, fa1, fb1);
+        for (int s = 0; s + 1 < SS; ++s) {
+          if (s % 2 == 0) {
+            frags(a_cur, b_cur, s + 1, fa1, fb1);
             mfmas(fa0, fb0);
-            if (s2 + 2 < SS) frags(ra[i], rb[i], s2 + 2, fa0, fb0);
+          } else {
+            frags(a_cur, b_cur, s + 1, fa0, fb0);
             mfmas(fa1, fb1);
           }
+          interleave_mfma<FM * FN, NFR, 0>();
+          __builtin_amdgcn_sched_barrier(0);
         }
+        __builtin_amdgcn_s_waitcnt(0);  // own loads of step kt + 1, own reads of slot kt
+        __builtin_amdgcn_s_barrier();
         __builtin_amdgcn_sched_barrier(0);
+        issue(kt + 2, a_cur, b_cur);
+        frags(a_nxt, b_nxt, 0, fa0, fb0);  // the last sub-step uses set 1
+        mfmas(fa1, fb1);
+        interleave_mfma<FM * FN, NFR, NLD>();
+        __builtin_amdgcn_sched_barrier(0);
+      };
+      issue(0, ra[0], rb[0]);
+      issue(1, ra[1], rb[1]);
+      wait_vmcnt<NLD>();
+      __builtin_amdgcn_s_barrier();
+      frags(ra[0], rb[0], 0, fa0, fb0);
+      // nk is even on this path: the loop body is one straight block, and at
+      // its head (from before the loop or from its end) only loads into
+      // slot 1 are in flight while slot 0 is read
+      for (int kg = 0; kg < nk; kg += 2) {
+        kstep(kg, ra[0], rb[0], ra[1], rb[1]);
+        kstep(kg + 1, ra[1], rb[1], ra[0], rb[0]);
+      }
+    } else {
+#pragma unroll
+      for (int st = 0; st < DL - 1; ++st) issue(st, ra[st], rb[st]);
+      for (int kg = 0; kg < nk; kg += DL) {
+#pragma unroll
+        for (int i = 0; i < DL; ++i) {
+          // all of step kg + i has landed once every wave is past the barrier,
+          // and everyone has finished reading slot i - 1 (one step ago)
+          wait_vmcnt<(DL - 2) * (IA + IB)>();
+          __builtin_amdgcn_s_barrier();
+          __builtin_amdgcn_sched_barrier(0);
+          issue(kg + i + DL - 1, ra[(i + DL - 1) % DL], rb[(i + DL - 1) % DL]);
+          if (kg + i < nk) {
+            frags(ra[i], rb[i], 0, fa0, fb0);
+#pragma unroll
+            for (int s2 = 0; s2 < SS; s2 += 2) {  // read sub-step s2 + 1 while s2 multiplies, and so on
+              frags(ra[i], rb[i], s2 + 1, fa1, fb1);
+              mfmas(fa0, fb0);
+              if (s2 + 2 < SS) frags(ra[i], rb[i], s2 + 2, fa0, fb0);
+              mfmas(fa1, fb1);
+            }
+          }
+          __builtin_amdgcn_sched_barrier(0);
+        }
       }
     }
     wait_vmcnt<0>();  // the ring's last loads land before the epilogue reuses LDS
@@ -613,6 +683,7 @@ static hipError_t launch_tile(const LinearArgs& a, hipStream_t s) {
   decltype(&linear_tile_kernel<DT, BM, BN, 0, BK, WGM, WGN, GM, DL>) k;
   if constexpr (DL != 0) {  // direct-load configurations need K a multiple of the step
     if ((a.K % BK) != 0) return hipErrorInvalidValue;
+    if (DL == 2 && (a.K / BK) % 2 != 0) return hipErrorInvalidValue;  // the 2-slot loop runs steps in pairs
     k = linear_tile_kernel<DT, BM, BN, 0, BK, WGM, WGN, GM, DL>;
   } else {
     k = (a.K % BK) == 0 ? linear_tile_kernel<DT, BM, BN, 0, BK, WGM, WGN, GM, 0>
@@ -635,10 +706,10 @@ static hipError_t launch_linear_t(const LinearArgs& a, hipStream_t s) {
         a.idx, a.n_idx, static_cast<uint16_t*>(a.out), a.acc, (int)a.T, (int)a.N, (int)a.K);
     return hipGetLastError();
   }
-  if (a.T >= 512 && a.N >= 512) {
+  if (a.T >= 512 && a.N >= 512 && a.K < (1 << 24)) {
     // direct loads: 128-byte steps in a 2-slot ring (whole cache lines per
     // row), else 64-byte steps in a 4-slot ring, else register staging
-    if (a.K % 128 == 0) return launch_tile<DT, 256, 256, 128, 4, 2, 4, 2>(a, s);
+    if (a.K % 256 == 0) return launch_tile<DT, 256, 256, 128, 4, 2, 4, 2>(a, s);  // an even step count
     if (a.K % 64 == 0) return launch_tile<DT, 256, 256, 64, 4, 2, 4, 4>(a, s);
     return launch_tile<DT, 256, 256, 64, 4, 2, 4, 0>(a, s);
   }
