@@ -65,6 +65,10 @@ SHAPES = [
     (1, 64, 64), (3, 24, 5), (8, 8, 4), (16, 4096, 130), (17, 520, 300), (33, 136, 65),
     (100, 264, 257), (130, 1000, 129), (257, 512, 513), (300, 136, 40), (64, 8, 1), (5, 100, 7),
     (2, 17, 3), (40, 37, 11), (600, 640, 520),
+    # large tiles: 128-byte steps in pairs (K % 256 == 0; two steps only at
+    # K = 256), 64-byte steps (K % 64 == 0), register staging (other K), each
+    # with ragged T and N tails
+    (600, 768, 520), (513, 256, 777), (512, 512, 512), (530, 520, 515), (515, 100, 520),
 ]
 
 
