@@ -54,6 +54,9 @@ def parse():
     p.add_argument("--settle-ms", type=float, default=200.0,
                    help="untimed steps run for this long before the warm-up, so the clocks have settled")
     p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--api", choices=["binding", "module", "graph"], default="binding",
+                   help="how a step is issued: the C-ABI binding, the Linear8bitLt module, "
+                        "or a HIP graph of the binding's launches captured once per input copy")
     p.add_argument("--copy-mib", type=float, default=0.0,
                    help="instead of the benchmark, run 10 plain device-to-device copies of this "
                         "many MiB (the calibration for HBM byte counters) and exit")
@@ -210,11 +213,48 @@ def main():
     ws = B.Workspace(T, K, N, X0.dtype, dev)
     out = torch.empty((T, N), dtype=X0.dtype, device=dev)
 
-    def step(i):
+    def bound_step(i):
         cp = copies[i % R]
         if case.weights_each_call:
             B.lli8_quant_weight_rowwise(cp["W"], cp["CB"], cp["SCB"])
         B.lli8_int8_linear(cp["X"], cp["CB"], cp["SCB"], cp["bias"], case.threshold, out=out, ws=ws)
+
+    step = bound_step
+    if args.api == "module":
+        # one Linear8bitLt per input copy, sharing nothing but the device
+        from bit_quantized_matmul_amd.nn import Linear8bitLt
+        layers = []
+        for cp in copies:
+            layer = Linear8bitLt(K, N, bias=cp["bias"] is not None, has_fp16_weights=case.weights_each_call,
+                                 threshold=case.threshold, device="meta", dtype=X0.dtype)
+            if case.weights_each_call:
+                layer.weight = torch.nn.Parameter(cp["W"], requires_grad=False)
+            else:
+                layer._set_int8(cp["CB"], cp["SCB"])
+            layer.bias = None if cp["bias"] is None else torch.nn.Parameter(cp["bias"], requires_grad=False)
+            layers.append(layer)
+
+        def step(i):
+            layers[i % R](copies[i % R]["X"])
+    elif args.api == "graph":
+        # the binding's launches of one step, captured once per input copy on a
+        # side stream (default priority) and replayed; the workspace and the
+        # output buffer are shared by every graph, as by the eager steps
+        graphs = []
+        cap = torch.cuda.Stream()
+        for _ in range(2):  # eager runs on the capture stream first
+            with torch.cuda.stream(cap):
+                bound_step(0)
+        torch.cuda.synchronize()
+        for r in range(R):
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g, stream=cap):
+                bound_step(r)
+            graphs.append(g)
+        torch.cuda.synchronize()
+
+        def step(i):
+            graphs[i % R].replay()
 
     # clocks: an idle GPU ramps up over tens of milliseconds; run untimed
     # steps until they have settled, then the W warm-up steps
@@ -227,6 +267,8 @@ def main():
         torch.cuda.synchronize()
     for i in range(args.warmup):
         step(i)
+    torch.cuda.synchronize()
+    bound_step(0)  # the binding's workspace holds the outlier count whatever the api
     torch.cuda.synchronize()
     n_idx = int(ws.n_idx.item())
 
@@ -243,11 +285,12 @@ def main():
     ms = e0.elapsed_time(e1) / args.steps
 
     # per-kernel durations: a second pass with events around each kernel
+    # (through the binding: events cannot be recorded inside a replayed graph)
     B.lli8_trace_enable(True)
     B.lli8_trace_read()
     kern_ms = {}
     for i in range(args.steps):
-        step(i)
+        bound_step(i)
         for name, kms in B.lli8_trace_read():
             kern_ms.setdefault(name, []).append(kms)
     torch.cuda.synchronize()
@@ -279,7 +322,7 @@ def main():
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 5),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "int8",
         "data": "synthetic",
-        "config": {"workload": args.workload, "T": T, "K": K, "N": N, "act_dtype": case.dtype,
+        "config": {"workload": args.workload, "api": args.api, "T": T, "K": K, "N": N, "act_dtype": case.dtype,
                    "threshold": case.threshold, "n_idx": n_idx, "bias": case.bias is not None,
                    "weights": "quantised every call" if case.weights_each_call else "pre-quantised",
                    "input_copies_rotated": R, "rotation_mib": round(R * copy_bytes / 2 ** 20, 1),

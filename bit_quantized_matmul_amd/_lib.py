@@ -136,10 +136,23 @@ def _ptr(t) -> Optional[int]:
     return t.data_ptr()
 
 
+_raw_stream = None
+
+
 def _stream(device, stream=None) -> int:
+    """The HIP stream to enqueue on: `stream`, else torch's current stream of
+    `device` (queried through torch's raw-handle accessor when it has one,
+    which costs a small fraction of building a Stream object)."""
+    global _raw_stream
     if stream is not None:
         return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
-    return _torch().cuda.current_stream(device).cuda_stream
+    torch = _torch()
+    if _raw_stream is None:
+        _raw_stream = getattr(torch._C, "_cuda_getCurrentRawStream", False)
+    if _raw_stream:
+        idx = device.index if device.index is not None else torch.cuda.current_device()
+        return _raw_stream(idx)
+    return torch.cuda.current_stream(device).cuda_stream
 
 
 def lli8_quant_weight_rowwise(W, CB=None, SCB=None, stream=None):
@@ -213,8 +226,7 @@ def lli8_int8_linear(X, CB, SCB, bias=None, threshold: float = 6.0, out=None,
     want_acc) of this call.
     """
     torch = _torch()
-    lead = X.shape[:-1]
-    X2 = X.reshape(-1, X.shape[-1])
+    X2 = X if X.dim() == 2 else X.reshape(-1, X.shape[-1])
     T, K = X2.shape
     N = CB.shape[0]
     if CB.shape[1] != K:
@@ -226,4 +238,4 @@ def lli8_int8_linear(X, CB, SCB, bias=None, threshold: float = 6.0, out=None,
     _check(lib().lli8_int8_linear(_ptr(X2), T, K, N, _dt(X2), _ptr(CB), _ptr(SCB), _ptr(bias),
                                   float(threshold), _ptr(out), ctypes.byref(ws._struct),
                                   _stream(X.device, stream)))
-    return out.reshape(*lead, N), ws
+    return (out if X.dim() == 2 else out.reshape(*X.shape[:-1], N)), ws

@@ -248,3 +248,36 @@ def test_every_column_an_outlier_skips_nothing_it_needs():
     g, r = _check_full(case, 0.01)
     assert g["n"] == case.K
     assert not g["acc"].any()
+
+
+@pytest.mark.parametrize("T,K,N", [(16, 4096, 512), (600, 768, 520)])
+def test_graph_replays_match_eager(T, K, N):
+    """The whole call captured in a HIP graph (torch.cuda.graph on a side
+    stream) and replayed several times, with eager calls on other inputs in
+    between: every replay equals the eager result on its own input."""
+    import torch
+    B = _lib()
+    ca, cb = random_case(T, K, N, seed=71, n_out=3), random_case(T, K, N, seed=72, n_out=5)
+    Xa, Xb = to_dev(ca.X, "f16"), to_dev(cb.X, "f16")
+    W = to_dev(ca.W, "f16")
+    bias = to_dev(ca.bias, "f16")
+    CB, SCB = B.lli8_quant_weight_rowwise(W)
+    ws = B.Workspace(T, K, N, torch.float16, "cuda")
+    out = torch.empty((T, N), dtype=torch.float16, device="cuda")
+    ref_a, _ = B.lli8_int8_linear(Xa, CB, SCB, bias, 6.0)
+    ref_b, _ = B.lli8_int8_linear(Xb, CB, SCB, bias, 6.0)
+    side = torch.cuda.Stream()
+    with torch.cuda.stream(side):
+        B.lli8_int8_linear(Xa, CB, SCB, bias, 6.0, out=out, ws=ws)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=side):
+        B.lli8_int8_linear(Xa, CB, SCB, bias, 6.0, out=out, ws=ws)
+    for _ in range(3):
+        out.zero_()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out, ref_a)
+        got_b, _ = B.lli8_int8_linear(Xb, CB, SCB, bias, 6.0, out=out, ws=ws)  # eager, same buffers
+        torch.cuda.synchronize()
+        assert torch.equal(got_b, ref_b)
