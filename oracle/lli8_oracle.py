@@ -48,6 +48,19 @@ reason, in the design notes of the repository):
   * The outlier product uses X unquantised and the recovered weight rounded to
     the activation dtype, in both weight modes.
 
+Vector-wise quantisation on its own (not a step of the forward; section
+"Quantization mechanics": zero-point and absmax, each row-wise or
+column-wise):
+  V1  absmax per row or per column: the O3-O5 quantiser without exclusions,
+      applied to X or to X transposed; the scale stored is the absmax.
+  V2  zero-point per row or per column.  Readings: the range is the vector's
+      [min, max] widened to contain 0 (so 0.0 has an exact code, the zero
+      point); nd = fl32(254 / fl32(hi - lo)); zp = round_half_away(fl32(-lo *
+      nd)) - 127, an integer in [-127, 127]; code = clamp(round_half_away(
+      fl32(x * nd)) + zp, -127, 127).  For [-1, 1] this is absmax with scale
+      127.  An all-zero vector gets nd = 0, zp = 0 and codes 0.  Stored: nd
+      (float32) and zp (int32); x is recovered as (code - zp) / nd.
+
 Parity pins: every step above is pinned by CPU tests (worked example, closed
 forms, brute force, invariants).  Parity unpinned: the exact bits of the final
 fp16/bf16 output, which the GPU path need only match within tolerance.
@@ -174,6 +187,67 @@ def quantize_activations(X: np.ndarray, threshold: float):
 def quantize_weight(W: np.ndarray):
     """O6: (CB int8 [N, K], SCB float32 [N]) for float32 weights W [N, K]."""
     return absmax_quantize_rows(W, None)
+
+
+# ------------------------------- V1-V2: vector-wise quantisation variants ----
+
+def absmax_quantize(X: np.ndarray, axis: int):
+    """V1: absmax codes with one scale per row (axis=1) or per column (axis=0).
+    Returns (codes int8 like X, absmax float32 [rows or columns])."""
+    X = np.asarray(X, dtype=np.float32)
+    if axis == 1:
+        return absmax_quantize_rows(X, None)
+    codes, amax = absmax_quantize_rows(X.T, None)
+    return np.ascontiguousarray(codes.T), amax
+
+
+def zeropoint_quantize_rows(X: np.ndarray):
+    """V2 per row: (codes int8 [R, C], nd float32 [R], zp int32 [R])."""
+    X = np.asarray(X, dtype=np.float32)
+    R, C = X.shape
+    if C == 0:
+        return np.zeros((R, 0), np.int8), np.zeros(R, np.float32), np.zeros(R, np.int32)
+    lo = np.minimum(X.min(axis=1), np.float32(0)).astype(np.float32)
+    hi = np.maximum(X.max(axis=1), np.float32(0)).astype(np.float32)
+    width = (hi - lo).astype(np.float32)                    # fl32(hi - lo)
+    nd = np.zeros(R, dtype=np.float32)
+    zp = np.zeros(R, dtype=np.int32)
+    codes = np.zeros((R, C), dtype=np.int8)
+    live = width > 0
+    if np.any(live):
+        nd[live] = np.float32(254) / width[live]              # fl32(254 / width)
+        zl = (-lo[live] * nd[live]).astype(np.float32)        # fl32(-lo * nd)
+        zp[live] = (round_half_away(zl) - 127).astype(np.int32)
+        v = X[live] * nd[live][:, None]                        # fl32(x * nd)
+        assert v.dtype == np.float32
+        q = np.clip(round_half_away(v) + zp[live][:, None], -INT8_MAX, INT8_MAX)
+        codes[live] = q.astype(np.int8)
+    return codes, nd, zp
+
+
+def zeropoint_quantize(X: np.ndarray, axis: int):
+    """V2 per row (axis=1) or per column (axis=0)."""
+    X = np.asarray(X, dtype=np.float32)
+    if axis == 1:
+        return zeropoint_quantize_rows(X)
+    codes, nd, zp = zeropoint_quantize_rows(X.T)
+    return np.ascontiguousarray(codes.T), nd, zp
+
+
+def absmax_dequantize(codes: np.ndarray, amax: np.ndarray, axis: int) -> np.ndarray:
+    """x^ = code * absmax / 127 (float64)."""
+    a = amax.astype(np.float64) / INT8_MAX
+    return codes.astype(np.float64) * (a[:, None] if axis == 1 else a[None, :])
+
+
+def zeropoint_dequantize(codes: np.ndarray, nd: np.ndarray, zp: np.ndarray, axis: int) -> np.ndarray:
+    """x^ = (code - zp) / nd (float64); 0 where nd = 0."""
+    n = nd.astype(np.float64)
+    inv = np.divide(1.0, n, out=np.zeros_like(n), where=n > 0)
+    z = zp.astype(np.float64)
+    if axis == 1:
+        return (codes.astype(np.float64) - z[:, None]) * inv[:, None]
+    return (codes.astype(np.float64) - z[None, :]) * inv[None, :]
 
 
 # --------------------------------------------------- O7: int8 accumulation ----
