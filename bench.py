@@ -54,6 +54,9 @@ def parse():
     p.add_argument("--settle-ms", type=float, default=200.0,
                    help="untimed steps run for this long before the warm-up, so the clocks have settled")
     p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--vectorwise", default="",
+                   help="SCHEME:AXIS (absmax|zeropoint : rows|cols): time lli8_quant_vectorwise on the "
+                        "workload's activation matrix instead of the forward")
     p.add_argument("--api", choices=["binding", "module", "graph"], default="binding",
                    help="how a step is issued: the C-ABI binding, the Linear8bitLt module, "
                         "or a HIP graph of the binding's launches captured once per input copy")
@@ -162,6 +165,79 @@ def cpu_baseline(case, CB_np, SCB_np, seconds):
                       + ("; weight quantisation included" if case.weights_each_call else "")}
 
 
+def bench_vectorwise(args):
+    """Vector-wise quantisation (absmax or zero-point, per row or per column)
+    of the workload's activation matrix X [T, K]: one JSON line, GB/s of the
+    algorithmic bytes (X read once, codes written once, one scale and zero
+    point per vector) against the HBM peak, with the oracle on the host beside it."""
+    import numpy as np
+    import torch
+    import bit_quantized_matmul_amd as B
+    from workloads import config_case
+    scheme, axis = args.vectorwise.split(":")
+    case = config_case(args.workload)
+    dev = torch.device("cuda:0")
+    X0 = torch.from_numpy(np.ascontiguousarray(case.X).view(np.int16)).view(
+        torch.float16 if case.dtype == "f16" else torch.bfloat16).to(dev)
+    R, C = X0.shape
+    nvec = R if axis == "rows" else C
+    copy_bytes = X0.numel() * 2
+    Rn = max(1, min(64, -(-int(args.rotate_mib * 2 ** 20) // copy_bytes)))
+    xs = [X0] + [X0.clone() for _ in range(Rn - 1)]
+    codes = torch.empty((R, C), dtype=torch.int8, device=dev)
+    scale = torch.empty((nvec,), dtype=torch.float32, device=dev)
+    zp = torch.empty((nvec,), dtype=torch.int32, device=dev)
+
+    def step(i):
+        B.lli8_quant_vectorwise(xs[i % Rn], scheme, axis, codes, scale, zp if scheme == "zeropoint" else None)
+
+    t0 = time.perf_counter()
+    n = 0
+    while (time.perf_counter() - t0) * 1e3 < args.settle_ms:
+        for _ in range(8):
+            step(n)
+            n += 1
+        torch.cuda.synchronize()
+    for i in range(args.warmup):
+        step(i)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record()
+    for i in range(args.steps):
+        step(i)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / args.steps
+    alg = R * C * 2 + R * C + nvec * (8 if scheme == "zeropoint" else 4)
+    gbs = alg / (ms * 1e-3) / 1e9
+    line = {"metric": f"vector-wise {scheme} quantisation per {axis[:-1]}, GB/s of algorithmic bytes",
+            "value": round(gbs, 2), "unit": "GB/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+            "ms_per_step": round(ms, 5), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+            "dtype": case.dtype, "data": "synthetic",
+            "config": {"workload": f"{args.workload} activations", "R": R, "C": C, "scheme": scheme,
+                       "axis": axis, "input_copies_rotated": Rn, "algorithmic_bytes": alg},
+            "roofline": {"bound": "hbm", "achieved": round(gbs, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                         "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None}}
+    if not args.no_cpu_baseline:
+        import oracle as O
+        Xf = O.decode_bits(case.X, case.dtype)
+        ax = 1 if axis == "rows" else 0
+        times = []
+        t_end = time.perf_counter() + args.cpu_seconds
+        while time.perf_counter() < t_end and len(times) < 20:
+            t = time.perf_counter()
+            if scheme == "zeropoint":
+                O.zeropoint_quantize(Xf, ax)
+            else:
+                O.absmax_quantize(Xf, ax)
+            times.append(time.perf_counter() - t)
+        tc = sum(times) / len(times)
+        line["cpu_baseline"] = {"value": round(alg / tc / 1e9, 3), "unit": "GB/s", "cores": 1, "kind": "oracle",
+                                "sample": f"full matrix (decoded to float32 beforehand); {len(times)} calls, "
+                                          f"mean {tc * 1e3:.1f} ms per call"}
+    print(json.dumps(line), flush=True)
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -170,6 +246,9 @@ def main():
         sys.exit(2)
     if args.copy_mib > 0:
         copy_calibration(args.copy_mib)
+        return
+    if args.vectorwise:
+        bench_vectorwise(args)
         return
 
     import numpy as np

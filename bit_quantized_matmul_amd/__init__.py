@@ -13,13 +13,13 @@ CPU fallback.
 from __future__ import annotations
 
 from ._lib import (LLI8_BF16, LLI8_F16, Lli8Error, Workspace, lib,  # noqa: F401
-                   library_path, lli8_int8_linear, lli8_quant_rowwise_outliers,
+                   library_path, lli8_int8_linear, lli8_quant_rowwise_outliers, lli8_quant_vectorwise,
                    lli8_quant_weight_rowwise, lli8_scratch_bytes, lli8_scratch_bytes_full, lli8_status_string,
                    lli8_trace_enable, lli8_trace_read, lli8_version)
 
 __all__ = [
     "LLI8_F16", "LLI8_BF16", "Lli8Error", "Workspace", "lib", "library_path",
-    "lli8_int8_linear", "lli8_quant_rowwise_outliers", "lli8_quant_weight_rowwise",
+    "lli8_int8_linear", "lli8_quant_rowwise_outliers", "lli8_quant_vectorwise", "lli8_quant_weight_rowwise",
     "lli8_scratch_bytes", "lli8_scratch_bytes_full", "lli8_status_string", "lli8_trace_enable", "lli8_trace_read",
     "lli8_version",
 ]

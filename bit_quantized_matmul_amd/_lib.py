@@ -10,6 +10,8 @@ LIB_NAME = "liblli8.so"
 
 LLI8_F16 = 0
 LLI8_BF16 = 1
+LLI8_ABSMAX, LLI8_ZEROPOINT = 0, 1   # lli8_scheme_t
+LLI8_ROWS, LLI8_COLS = 0, 1          # lli8_axis_t
 
 STATUS = {0: "LLI8_OK", 1: "LLI8_ERR_NULL", 2: "LLI8_ERR_SHAPE", 3: "LLI8_ERR_DTYPE",
           4: "LLI8_ERR_ALIGN", 5: "LLI8_ERR_THRESHOLD", 6: "LLI8_ERR_UNSUPPORTED",
@@ -73,6 +75,8 @@ def lib() -> ctypes.CDLL:
     L.lli8_int8_linear.argtypes = [vp, i64, i64, i64, i32, vp, vp, vp, f32, vp,
                                    ctypes.POINTER(_Workspace), vp]
     L.lli8_int8_linear.restype = i32
+    L.lli8_quant_vectorwise.argtypes = [vp, i64, i64, i32, i32, i32, vp, vp, vp, vp]
+    L.lli8_quant_vectorwise.restype = i32
     L.lli8_scratch_bytes.argtypes = [i64, i64, i32]
     L.lli8_scratch_bytes.restype = ctypes.c_size_t
     L.lli8_scratch_bytes_full.argtypes = [i64, i64, i64, i32]
@@ -184,6 +188,32 @@ def lli8_quant_rowwise_outliers(X, threshold: float, CA=None, SCA=None, bitmap=N
                                              _ptr(SCA), _ptr(bitmap), _ptr(idx), _ptr(n_idx),
                                              _stream(dev, stream)))
     return CA, SCA, bitmap, idx, n_idx
+
+
+def lli8_quant_vectorwise(X, scheme: str = "absmax", axis: str = "rows", codes=None, scale=None,
+                          zero_point=None, stream=None):
+    """X [R, C] fp16/bf16 -> (codes int8 [R, C], scale fp32, zero_point int32 or None),
+    one scale per row (axis="rows") or per column (axis="cols"); scheme
+    "absmax" (scale = max |x|) or "zeropoint" (scale = 254 / width of the
+    range widened to contain 0, zero_point = the code of 0.0)."""
+    torch = _torch()
+    if scheme not in ("absmax", "zeropoint") or axis not in ("rows", "cols"):
+        raise ValueError(f"scheme {scheme!r} / axis {axis!r}")
+    if X.dim() != 2:
+        raise ValueError("X must be 2-D [R, C]")
+    R, C = X.shape
+    nvec = R if axis == "rows" else C
+    dev = X.device
+    codes = torch.empty((R, C), dtype=torch.int8, device=dev) if codes is None else codes
+    scale = torch.empty((nvec,), dtype=torch.float32, device=dev) if scale is None else scale
+    zp = None
+    if scheme == "zeropoint":
+        zp = torch.empty((nvec,), dtype=torch.int32, device=dev) if zero_point is None else zero_point
+    _check(lib().lli8_quant_vectorwise(_ptr(X), R, C, _dt(X),
+                                       LLI8_ZEROPOINT if scheme == "zeropoint" else LLI8_ABSMAX,
+                                       LLI8_ROWS if axis == "rows" else LLI8_COLS,
+                                       _ptr(codes), _ptr(scale), _ptr(zp), _stream(dev, stream)))
+    return codes, scale, zp
 
 
 class Workspace:

@@ -195,6 +195,29 @@ lli8_status_t lli8_quant_weight_rowwise(const void* W, int64_t N, int64_t K, lli
   return LLI8_OK;
 }
 
+lli8_status_t lli8_quant_vectorwise(const void* X, int64_t R, int64_t C, lli8_dtype_t dtype,
+                                    lli8_scheme_t scheme, lli8_axis_t axis, int8_t* codes,
+                                    float* scale, int32_t* zero_point, void* stream) {
+  TRY(check_dtype(dtype));
+  if (scheme != LLI8_ABSMAX && scheme != LLI8_ZEROPOINT)
+    return fail(LLI8_ERR_UNSUPPORTED, "unknown scheme %d", (int)scheme);
+  if (axis != LLI8_ROWS && axis != LLI8_COLS) return fail(LLI8_ERR_UNSUPPORTED, "unknown axis %d", (int)axis);
+  if (R < 0 || C < 0) return fail(LLI8_ERR_SHAPE, "bad sizes R=%lld C=%lld", (long long)R, (long long)C);
+  const int64_t nvec = axis == LLI8_ROWS ? R : C;
+  if (nvec == 0) return LLI8_OK;
+  if (R > 0 && C > 0) {
+    REQUIRE(X, "X");
+    REQUIRE(codes, "codes");
+  }
+  REQUIRE(scale, "scale");
+  if (scheme == LLI8_ZEROPOINT) REQUIRE(zero_point, "zero_point");
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  TRACED(s, scheme == LLI8_ZEROPOINT ? "quant_zeropoint" : "quant_absmax",
+         lli8::launch_quant_vectorwise((int)dtype, X, R, C, scheme == LLI8_ZEROPOINT ? 1 : 0,
+                                       axis == LLI8_ROWS ? 0 : 1, codes, scale, zero_point, s));
+  return LLI8_OK;
+}
+
 lli8_status_t lli8_quant_rowwise_outliers(const void* X, int64_t T, int64_t K, lli8_dtype_t dtype, float threshold,
                                           int8_t* CA, float* SCA, uint32_t* bitmap, int32_t* idx, int32_t* n_idx,
                                           void* stream) {

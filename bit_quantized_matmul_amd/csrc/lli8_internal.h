@@ -20,6 +20,8 @@ hipError_t launch_quant_act(int dt, const void* X, int64_t T, int64_t K, const u
 
 // Recovered weights of the first min(ceil(n/32), chunks) outlier chunks,
 // chunk-major [chunk][N][32] 16-bit (n read on the device).
+hipError_t launch_quant_vectorwise(int dt, const void* X, int64_t R, int64_t C, int zeropoint, int axis,
+                                   int8_t* codes, float* scale, int32_t* zp, hipStream_t s);
 hipError_t launch_recover_outliers(int dt, const int8_t* CB, const float* SCB, int64_t N, int64_t K,
                                    const int32_t* idx, const int32_t* n_idx, void* wo, int chunks, hipStream_t s);
 

@@ -150,6 +150,35 @@ lli8_status_t lli8_int8_linear(const void* X, int64_t T, int64_t K, int64_t N,
                                const lli8_workspace_t* ws, void* stream);
 
 /*
+ * Vector-wise quantisation of a 16-bit matrix on its own ("Hugging Face
+ * integrates LLM.int8() ...", section "Quantization mechanics": zero-point and
+ * absmax, each row-wise or column-wise).  Not a step of lli8_int8_linear.
+ *   X      [R, C] fp16/bf16 row-major (read)
+ *   codes  [R, C] int8 (written)
+ *   scale  [R] (axis LLI8_ROWS) or [C] (axis LLI8_COLS) fp32 (written)
+ *   zero_point  same count, int32 (written; zero-point scheme only, may be
+ *          NULL for absmax)
+ * LLI8_ABSMAX: scale = max |x| of the vector, code = round_half_away(
+ *   fl32(x * fl32(127 / scale))) in [-127, 127]; an all-zero vector gets
+ *   scale 0 and codes 0.  x is recovered as code * scale / 127.
+ * LLI8_ZEROPOINT: the vector's range [min, max] widened to contain 0 is
+ *   mapped onto [-127, 127]: scale = nd = fl32(254 / fl32(hi - lo)),
+ *   zero_point = round_half_away(fl32(-lo * nd)) - 127 (the code of 0.0),
+ *   code = clamp(round_half_away(fl32(x * nd)) + zero_point, -127, 127); an
+ *   all-zero vector gets nd 0, zero point 0, codes 0.  x is recovered as
+ *   (code - zero_point) / nd.
+ * Inputs are finite.  Asynchronous on `stream`; pointers 16-byte aligned.
+ * Errors: LLI8_ERR_NULL, _SHAPE (R or C negative), _DTYPE, _ALIGN, and
+ * LLI8_ERR_UNSUPPORTED for an unknown scheme or axis, before anything is
+ * enqueued.
+ */
+typedef enum { LLI8_ABSMAX = 0, LLI8_ZEROPOINT = 1 } lli8_scheme_t;
+typedef enum { LLI8_ROWS = 0, LLI8_COLS = 1 } lli8_axis_t;
+lli8_status_t lli8_quant_vectorwise(const void* X, int64_t R, int64_t C, lli8_dtype_t dtype,
+                                    lli8_scheme_t scheme, lli8_axis_t axis, int8_t* codes,
+                                    float* scale, int32_t* zero_point, void* stream);
+
+/*
  * Optional kernel timing, for profiling.  While enabled (process-wide), each
  * kernel the entry points enqueue is bracketed by two HIP events recorded on
  * the call's stream.  lli8_trace_read waits for those events and reports the

@@ -96,6 +96,27 @@ def test_validation_activation_split():
         assert f(*bad) == 4
 
 
+def test_validation_vectorwise():
+    L = _lib().lib()
+    f = L.lli8_quant_vectorwise
+    args = [FAKE, 4, 8, 0, 1, 0, FAKE, FAKE, FAKE, None]
+    assert f(*args[:3], 5, *args[4:]) == 3                      # dtype
+    assert f(*args[:4], 2, *args[5:]) == 6                      # scheme
+    assert f(*args[:5], 3, *args[6:]) == 6                      # axis
+    assert f(FAKE, -1, 8, 0, 1, 0, FAKE, FAKE, FAKE, None) == 2  # R < 0
+    assert f(FAKE, 4, -8, 0, 1, 0, FAKE, FAKE, FAKE, None) == 2  # C < 0
+    for pos in (0, 6, 7, 8):
+        bad = list(args); bad[pos] = None
+        assert f(*bad) == 1
+        bad = list(args); bad[pos] = FAKE + 8
+        assert f(*bad) == 4
+    absmax = list(args); absmax[4] = 0; absmax[8] = None          # no zero point for absmax: allowed
+    absmax[0] = None                                              # ... but X is still required
+    assert f(*absmax) == 1
+    assert f(FAKE, 0, 8, 0, 1, 0, FAKE, FAKE, FAKE, None) == 0    # no rows: a no-op
+    assert f(FAKE, 4, 0, 0, 1, 1, FAKE, FAKE, FAKE, None) == 0    # no columns, column-wise: a no-op
+
+
 def test_validation_linear():
     Lm = _lib()
     L = Lm.lib()

@@ -174,3 +174,20 @@ def random_case(T, K, N, dtype=F16, seed=0, n_out=3, bias="normal",
     return make_case(f"rand_{T}x{K}x{N}_{dtype}_{seed}", T, K, N, dtype,
                      n_out=n_out, out_lo=out_lo, out_hi=out_hi, bias=bias,
                      threshold=threshold, seed=seed)
+
+
+def matrix_bits(R: int, C: int, dtype: str = F16, seed: int = 0) -> np.ndarray:
+    """A 16-bit matrix [R, C] (raw bits) with rows of varied range: each row
+    N(0, 1) times a row scale U(0.01, 30) plus a row offset U(-5, 5); every
+    7th row made non-negative, every 9th (from 1) non-positive, every 11th
+    (from 2) all zero, column 3 (when present) exactly zero."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    x = rng.standard_normal((R, C), dtype=np.float32)
+    x *= rng.uniform(0.01, 30.0, size=(R, 1)).astype(np.float32)
+    x += rng.uniform(-5.0, 5.0, size=(R, 1)).astype(np.float32)
+    x[::7] = np.abs(x[::7])
+    x[1::9] = -np.abs(x[1::9])
+    x[2::11] = 0.0
+    if C > 3:
+        x[:, 3] = 0.0
+    return _f32_to_bits(x, dtype)
