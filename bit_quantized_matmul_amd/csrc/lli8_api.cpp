@@ -286,10 +286,11 @@ lli8_status_t lli8_int8_linear(const void* X, int64_t T, int64_t K, int64_t N, l
     TRACED(s, "decode_fused", lli8::launch_decode_fused(f, s));
     return LLI8_OK;
   }
-  // room for recovered outlier weights after the gathered columns (tile path only)
+  // room for recovered outlier weights after the gathered columns (tile path
+  // only: the weight-streaming kernel for T <= 64, K % 16 == 0 reads CB itself)
   void* wo = nullptr;
   int wo_chunks = 0;
-  if (outl && T > 16) {
+  if (outl && (T > 64 || (K % 16) != 0)) {
     const size_t xb = xo_bytes(T, K), per_chunk = (size_t)N * 64;
     const size_t room = ws->scratch_bytes > xb ? ws->scratch_bytes - xb : 0;
     const int64_t c = (int64_t)(room / per_chunk), cmax = (K + 31) / 32;

@@ -20,9 +20,10 @@
 //     fp32 in place (same 32x32 register layout), then runs the outlier
 //     columns through v_mfma_f32_32x32x16_{f16,bf16} on the same registers,
 //     then adds the bias and rounds once to the output dtype.
-//   * decode kernel (T <= 16): a streaming kernel; each workgroup owns 16
+//   * weight-streaming kernel (T <= 64, K % 16 == 0): each workgroup owns 16
 //     output features and reads their int8 weight rows once with 16-byte
-//     loads, four waves splitting K, v_mfma_i32_16x16x64_i8.
+//     loads, four waves splitting K, v_mfma_i32_16x16x64_i8 per block of 16
+//     tokens.
 #include "lli8_device.h"
 #include "lli8_internal.h"
 
@@ -608,72 +609,100 @@ __global__ __launch_bounds__(64 * WGM * WGN) void linear_tile_kernel(
 }
 
 // ---------------------------------------------------------------- decode ----
-// T <= 16, K % 16 == 0.  Workgroup = 16 output features; wave w takes the
+// T <= 16 MB, K % 16 == 0.  Workgroup = 16 output features; wave w takes the
 // 256-byte K slices w, w + 4, ...; lane (n, g) = (lane % 16, lane / 16) loads
-// 64 contiguous bytes of weight row n and the matching activation bytes, which
-// feed four 16x16x64 MFMAs (A and B use the same K permutation, so the dot
-// products are exact).  Partial int32 tiles are summed through LDS in a fixed
-// order (deterministic).
-template <int DT>
+// 64 contiguous bytes of weight row n once and, for each block of 16 tokens,
+// the matching activation bytes, which feed four 16x16x64 MFMAs per block (A
+// and B use the same K permutation, so the dot products are exact).  The
+// weight rows are streamed once whatever T is; N / 16 workgroups fill the
+// chip.  Partial int32 tiles are summed through LDS in a fixed order
+// (deterministic).
+template <int DT, int MB>
 __global__ __launch_bounds__(256) void linear_decode_kernel(
     const int8_t* __restrict__ CA, const int8_t* __restrict__ CB, const float* __restrict__ SCA,
     const float* __restrict__ SCB, const uint16_t* __restrict__ bias, const uint16_t* __restrict__ xo,
     const int32_t* __restrict__ idx, const int32_t* __restrict__ n_idx_p, uint16_t* __restrict__ out,
     int32_t* __restrict__ acc_out, int T, int N, int K) {
-  __shared__ v4i red[3][64];
+  __shared__ v4i red[3][MB][64];
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int64_t n0 = (int64_t)blockIdx.x * 16;
   const int nr = lane & 15, g = lane >> 4;
   const int64_t n = n0 + nr;
   const int nss = (K + 255) >> 8;
-  v4i acc = {0, 0, 0, 0};
+  v4i acc[MB];
+#pragma unroll
+  for (int mb = 0; mb < MB; ++mb) acc[mb] = (v4i){0, 0, 0, 0};
   const int8_t* brow = CB + n * (int64_t)K;
-  const int8_t* arow = CA + (int64_t)nr * K;
   for (int s = w; s < nss; s += 4) {
     const int64_t kb = (int64_t)s * 256 + g * 64;
-    u32x4 a[4], b[4];
+    u32x4 b[4];
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
       const int64_t k = kb + 16 * u;
       b[u] = (n < N && k < K) ? __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(brow + k))
                               : (u32x4){0u, 0u, 0u, 0u};
-      a[u] = (nr < T && k < K) ? *reinterpret_cast<const u32x4*>(arow + k) : (u32x4){0u, 0u, 0u, 0u};
     }
 #pragma unroll
-    for (int u = 0; u < 4; ++u)
-      acc = __builtin_amdgcn_mfma_i32_16x16x64_i8(__builtin_bit_cast(v4i, a[u]), __builtin_bit_cast(v4i, b[u]),
-                                                  acc, 0, 0, 0);
+    for (int mb = 0; mb < MB; ++mb) {
+      const int t = 16 * mb + nr;
+      const int8_t* arow = CA + (int64_t)t * K;
+      u32x4 a[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int64_t k = kb + 16 * u;
+        a[u] = (t < T && k < K) ? *reinterpret_cast<const u32x4*>(arow + k) : (u32x4){0u, 0u, 0u, 0u};
+      }
+#pragma unroll
+      for (int u = 0; u < 4; ++u)
+        acc[mb] = __builtin_amdgcn_mfma_i32_16x16x64_i8(__builtin_bit_cast(v4i, a[u]), __builtin_bit_cast(v4i, b[u]),
+                                                        acc[mb], 0, 0, 0);
+    }
   }
-  if (w > 0) red[w - 1][lane] = acc;
+  if (w > 0) {
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb) red[w - 1][mb][lane] = acc[mb];
+  }
   __syncthreads();
   if (w != 0) return;
-  acc += red[0][lane];
-  acc += red[1][lane];
-  acc += red[2][lane];
+#pragma unroll
+  for (int mb = 0; mb < MB; ++mb) {
+    acc[mb] += red[0][mb][lane];
+    acc[mb] += red[1][mb][lane];
+    acc[mb] += red[2][mb][lane];
+  }
 
-  // 16x16 accumulator layout: lane holds column lane % 16, rows 4 * (lane / 16) + r.
+  // 16x16 accumulator layout: lane holds column lane % 16, rows 4 * (lane / 16) + r
+  // of its block of 16 tokens.
   const int n_idx = *n_idx_p;
   const int64_t col = n0 + (lane & 15);
   if (col >= N) return;
   const float scb = SCB[col];
   const float bv = (bias != nullptr) ? to_f32<DT>(bias[col]) : 0.0f;
-  float o[4] = {0.f, 0.f, 0.f, 0.f};
+  float o[MB][4];
+#pragma unroll
+  for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) o[mb][r] = 0.0f;
   for (int p = 0; p < n_idx; ++p) {
     const float wv = to_f32<DT>(recover_w<DT>(CB[col * K + idx[p]], scb));
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int t = 4 * (lane >> 4) + r;
-      if (t < T) o[r] += to_f32<DT>(xo[((int64_t)(p >> 5) * T + t) * 32 + (p & 31)]) * wv;
-    }
+    for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int t = 16 * mb + 4 * (lane >> 4) + r;
+        if (t < T) o[mb][r] += to_f32<DT>(xo[((int64_t)(p >> 5) * T + t) * 32 + (p & 31)]) * wv;
+      }
   }
 #pragma unroll
-  for (int r = 0; r < 4; ++r) {
-    const int t = 4 * (lane >> 4) + r;
-    if (t >= T) continue;
-    if (acc_out != nullptr) acc_out[(int64_t)t * N + col] = acc[r];
-    const float d = (float)acc[r] * (SCA[t] * (scb * (1.0f / 16129.0f)));
-    out[(int64_t)t * N + col] = from_f32<DT>(d + o[r] + bv);
-  }
+  for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int t = 16 * mb + 4 * (lane >> 4) + r;
+      if (t >= T) continue;
+      if (acc_out != nullptr) acc_out[(int64_t)t * N + col] = acc[mb][r];
+      const float d = (float)acc[mb][r] * (SCA[t] * (scb * (1.0f / 16129.0f)));
+      out[(int64_t)t * N + col] = from_f32<DT>(d + o[mb][r] + bv);
+    }
 }
 
 template <int DT, int BM, int BN, int BK, int WGM, int WGN, int GM = 8, int DL = 0>
@@ -699,9 +728,13 @@ static hipError_t launch_tile(const LinearArgs& a, hipStream_t s) {
 
 template <int DT>
 static hipError_t launch_linear_t(const LinearArgs& a, hipStream_t s) {
-  if (a.T <= 16 && (a.K % 16) == 0) {
+  if (a.T <= 64 && (a.K % 16) == 0) {
+    // weight-streaming kernel: every weight row read once, N / 16 workgroups
     const int nb = (int)((a.N + 15) / 16);
-    linear_decode_kernel<DT><<<dim3(nb), dim3(256), 0, s>>>(
+    decltype(&linear_decode_kernel<DT, 1>) k = a.T <= 16 ? linear_decode_kernel<DT, 1>
+                                              : a.T <= 32 ? linear_decode_kernel<DT, 2>
+                                                          : linear_decode_kernel<DT, 4>;
+    k<<<dim3(nb), dim3(256), 0, s>>>(
         a.CA, a.CB, a.SCA, a.SCB, static_cast<const uint16_t*>(a.bias), static_cast<const uint16_t*>(a.xo),
         a.idx, a.n_idx, static_cast<uint16_t*>(a.out), a.acc, (int)a.T, (int)a.N, (int)a.K);
     return hipGetLastError();

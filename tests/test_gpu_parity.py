@@ -69,6 +69,8 @@ SHAPES = [
     # K = 256), 64-byte steps (K % 64 == 0), register staging (other K), each
     # with ragged T and N tails
     (600, 768, 520), (513, 256, 777), (512, 512, 512), (530, 520, 515), (515, 100, 520),
+    # 16 < T <= 64 with K % 16 == 0: the weight-streaming kernel, 2 or 4 token blocks
+    (17, 512, 300), (32, 4096, 520), (33, 256, 65), (48, 2048, 1000), (64, 1024, 130),
 ]
 
 
