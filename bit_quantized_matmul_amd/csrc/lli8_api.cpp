@@ -287,10 +287,10 @@ lli8_status_t lli8_int8_linear(const void* X, int64_t T, int64_t K, int64_t N, l
     return LLI8_OK;
   }
   // room for recovered outlier weights after the gathered columns (tile path
-  // only: the weight-streaming kernel for T <= 64, K % 16 == 0 reads CB itself)
+  // only: the weight-streaming kernel reads CB itself)
   void* wo = nullptr;
   int wo_chunks = 0;
-  if (outl && (T > 64 || (K % 16) != 0)) {
+  if (outl && (T > lli8::LLI8_STREAM_MAX_T || (K % 16) != 0)) {
     const size_t xb = xo_bytes(T, K), per_chunk = (size_t)N * 64;
     const size_t room = ws->scratch_bytes > xb ? ws->scratch_bytes - xb : 0;
     const int64_t c = (int64_t)(room / per_chunk), cmax = (K + 31) / 32;

@@ -20,7 +20,7 @@
 //     fp32 in place (same 32x32 register layout), then runs the outlier
 //     columns through v_mfma_f32_32x32x16_{f16,bf16} on the same registers,
 //     then adds the bias and rounds once to the output dtype.
-//   * weight-streaming kernel (T <= 64, K % 16 == 0): each workgroup owns 16
+//   * weight-streaming kernel (T <= 128, K % 16 == 0): each workgroup owns 16
 //     output features and reads their int8 weight rows once with 16-byte
 //     loads, four waves splitting K, v_mfma_i32_16x16x64_i8 per block of 16
 //     tokens.
@@ -728,12 +728,13 @@ static hipError_t launch_tile(const LinearArgs& a, hipStream_t s) {
 
 template <int DT>
 static hipError_t launch_linear_t(const LinearArgs& a, hipStream_t s) {
-  if (a.T <= 64 && (a.K % 16) == 0) {
+  if (a.T <= LLI8_STREAM_MAX_T && (a.K % 16) == 0) {
     // weight-streaming kernel: every weight row read once, N / 16 workgroups
     const int nb = (int)((a.N + 15) / 16);
     decltype(&linear_decode_kernel<DT, 1>) k = a.T <= 16 ? linear_decode_kernel<DT, 1>
                                               : a.T <= 32 ? linear_decode_kernel<DT, 2>
-                                                          : linear_decode_kernel<DT, 4>;
+                                              : a.T <= 64 ? linear_decode_kernel<DT, 4>
+                                                          : linear_decode_kernel<DT, 8>;
     k<<<dim3(nb), dim3(256), 0, s>>>(
         a.CA, a.CB, a.SCA, a.SCB, static_cast<const uint16_t*>(a.bias), static_cast<const uint16_t*>(a.xo),
         a.idx, a.n_idx, static_cast<uint16_t*>(a.out), a.acc, (int)a.T, (int)a.N, (int)a.K);
@@ -746,6 +747,9 @@ static hipError_t launch_linear_t(const LinearArgs& a, hipStream_t s) {
     if (a.K % 64 == 0) return launch_tile<DT, 256, 256, 64, 4, 2, 4, 4>(a, s);
     return launch_tile<DT, 256, 256, 64, 4, 2, 4, 0>(a, s);
   }
+  // 128 x 128 tiles unless they leave most of the chip idle; then 64 x 64
+  const int64_t t128 = ((a.T + 127) / 128) * ((a.N + 127) / 128);
+  if (t128 < 256) return launch_tile<DT, 64, 64, 64, 2, 2>(a, s);
   return launch_tile<DT, 128, 128, 64, 2, 2>(a, s);
 }
 

@@ -20,6 +20,10 @@ hipError_t launch_quant_act(int dt, const void* X, int64_t T, int64_t K, const u
 
 // Recovered weights of the first min(ceil(n/32), chunks) outlier chunks,
 // chunk-major [chunk][N][32] 16-bit (n read on the device).
+// Largest T the weight-streaming GEMM kernel takes (K % 16 == 0); above it
+// the tile kernel runs and reads recovered outlier weights from scratch.
+constexpr int64_t LLI8_STREAM_MAX_T = 128;
+
 hipError_t launch_quant_vectorwise(int dt, const void* X, int64_t R, int64_t C, int zeropoint, int axis,
                                    int8_t* codes, float* scale, int32_t* zp, hipStream_t s);
 hipError_t launch_recover_outliers(int dt, const int8_t* CB, const float* SCB, int64_t N, int64_t K,

@@ -69,8 +69,11 @@ SHAPES = [
     # K = 256), 64-byte steps (K % 64 == 0), register staging (other K), each
     # with ragged T and N tails
     (600, 768, 520), (513, 256, 777), (512, 512, 512), (530, 520, 515), (515, 100, 520),
-    # 16 < T <= 64 with K % 16 == 0: the weight-streaming kernel, 2 or 4 token blocks
+    # 16 < T <= 128 with K % 16 == 0: the weight-streaming kernel, 2, 4 or 8 token blocks
     (17, 512, 300), (32, 4096, 520), (33, 256, 65), (48, 2048, 1000), (64, 1024, 130),
+    (65, 512, 100), (128, 4096, 260), (100, 1040, 33),
+    # T < 512 with at least 256 tiles of 128 x 128: the 128 x 128 tile path (others take 64 x 64)
+    (300, 256, 11000),
 ]
 
 
