@@ -9,19 +9,20 @@
 // transformers") and the two results are summed.
 //
 // Two kernels:
-//   * tile kernel: BM x BN output tile per workgroup of WGM x WGN waves
-//     (256 x 256 on 4 x 2 waves: two waves per SIMD, so one wave's LDS and
-//     barrier waits overlap the other's MFMAs).  K is staged through LDS:
-//     for the large tiles with global_load_lds straight from memory into a
-//     ring of LDS slots (128-byte steps, two slots, so every row read is a
-//     whole cache line; 64-byte steps in four slots when K % 128 != 0),
-//     otherwise through registers 64 bytes at a time, double buffered, with
-//     v_mfma_i32_32x32x32_i8.  The epilogue turns the int32 accumulators into
-//     fp32 in place (same 32x32 register layout), then runs the outlier
-//     columns through v_mfma_f32_32x32x16_{f16,bf16} on the same registers,
-//     then adds the bias and rounds once to the output dtype.
-//   * weight-streaming kernel (T <= 128, K % 16 == 0): each workgroup owns 16
-//     output features and reads their int8 weight rows once with 16-byte
+//   * tile kernel: BM x BN output tile per workgroup of WGM x WGN waves.
+//     Large problems (T, N >= 512): 256 x 256 on 4 x 2 waves (two per SIMD),
+//     K straight from memory into LDS with global_load_lds: 128-byte steps
+//     in a 2-slot ring (K % 256 == 0; the step's barrier sits before its last
+//     sub-step's MFMAs, and each sub-step's LDS operand reads interleave with
+//     the previous sub-step's MFMAs), 64-byte steps in a 4-slot ring (K % 64
+//     == 0), else register-staged 64-byte steps.  Smaller problems: 128 x 128
+//     or 64 x 64 tiles on 2 x 2 waves, register-staged.  v_mfma_i32_32x32x32_i8
+//     throughout.  The epilogue turns the int32 accumulators into fp32 in
+//     place (same 32x32 register layout), runs the outlier columns through
+//     v_mfma_f32_32x32x16_{f16,bf16} on the same registers, then adds the
+//     bias and rounds once to the output dtype.
+//   * weight-streaming kernel (T <= 128, K % 16 == 0): each workgroup owns
+//     16 output features and reads their int8 weight rows once with 16-byte
 //     loads, four waves splitting K, v_mfma_i32_16x16x64_i8 per block of 16
 //     tokens.
 #include "lli8_device.h"
@@ -104,8 +105,9 @@ __device__ __forceinline__ void interleave_mfma() {
 }
 
 // DL = 0: global loads staged through registers, LDS double buffered (any K).
-// DL = D >= 3 (K % 64 == 0 only): loads go straight from global memory into a
-// D-stage LDS ring, D - 1 steps ahead.
+// DL = 2 (K a multiple of 2 BK): loads go straight from global memory into two
+// LDS slots, two steps in flight, steps run in pairs.
+// DL = D >= 3 (K % BK == 0): straight into a D-slot LDS ring, D - 1 steps ahead.
 template <int DT, int BM, int BN, int KM, int BK, int WGM, int WGN, int GM, int DL>
 __global__ __launch_bounds__(64 * WGM * WGN) void linear_tile_kernel(
     const int8_t* __restrict__ CA, const int8_t* __restrict__ CB, const float* __restrict__ SCA,
