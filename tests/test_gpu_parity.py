@@ -286,3 +286,15 @@ def test_graph_replays_match_eager(T, K, N):
         got_b, _ = B.lli8_int8_linear(Xb, CB, SCB, bias, 6.0, out=out, ws=ws)  # eager, same buffers
         torch.cuda.synchronize()
         assert torch.equal(got_b, ref_b)
+
+
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+@pytest.mark.parametrize("T,K,N,n_out,tau", [
+    (600, 512, 520, 150, 6.0),    # 5 outlier chunks: 4 through the 2-slot pipeline, 1 through the ring
+    (520, 768, 530, 0, 0.01),     # every column an outlier: 24 chunks, all through the pipeline
+    (512, 1024, 512, 260, 6.0),   # 9 chunks: 8 + 1
+])
+def test_many_outlier_chunks_large_tiles(T, K, N, n_out, tau, dtype):
+    case = random_case(T, K, N, dtype=dtype, seed=T + K + n_out, n_out=n_out)
+    g, r = _check_full(case, tau)
+    assert g["n"] >= min(n_out, K) and (tau > 0.1 or g["n"] == K)
