@@ -50,6 +50,21 @@ __device__ __forceinline__ uint16_t recover_w(int8_t cb, float scb) {
   return from_f32<DT>(p / 127.0f);
 }
 
+// Two fp32 values rounded (to nearest even) to the 16-bit dtype and packed,
+// the first in the low half (v_cvt_pk_f16_f32 / v_cvt_pk_bf16_f32).
+template <int DT>
+__device__ __forceinline__ uint32_t pack2(float lo, float hi) {
+  typedef float f2 __attribute__((ext_vector_type(2)));
+  const f2 v = {lo, hi};
+  if constexpr (DT == DT_F16) {
+    typedef _Float16 h2 __attribute__((ext_vector_type(2)));
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, h2));
+  } else {
+    typedef __bf16 b2 __attribute__((ext_vector_type(2)));
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, b2));
+  }
+}
+
 template <int DT>
 __device__ __forceinline__ v16f mfma16(const u32x4& a, const u32x4& b, const v16f& c) {
   if constexpr (DT == DT_F16)
@@ -108,7 +123,9 @@ __device__ __forceinline__ void interleave_mfma() {
 // DL = 2 (K a multiple of 2 BK): loads go straight from global memory into two
 // LDS slots, two steps in flight, steps run in pairs.
 // DL = D >= 3 (K % BK == 0): straight into a D-slot LDS ring, D - 1 steps ahead.
-template <int DT, int BM, int BN, int KM, int BK, int WGM, int WGN, int GM, int DL>
+// FL = 1: every tile lies wholly inside the output (T % BM == 0, N % BN ==
+// 0, N even), and the epilogue drops its bounds checks.
+template <int DT, int BM, int BN, int KM, int BK, int WGM, int WGN, int GM, int DL, int FL>
 __global__ __launch_bounds__(64 * WGM * WGN) void linear_tile_kernel(
     const int8_t* __restrict__ CA, const int8_t* __restrict__ CB, const float* __restrict__ SCA,
     const float* __restrict__ SCB, const uint16_t* __restrict__ bias, const uint16_t* __restrict__ xo,
@@ -449,25 +466,48 @@ __global__ __launch_bounds__(64 * WGM * WGN) void linear_tile_kernel(
       __builtin_amdgcn_sched_barrier(0);
     }
   }
-  // Dequantise in place: the fp32 value reuses the int32 accumulator's
-  // registers (the f32 and i32 32x32 MFMAs share one register layout).
-  float sb[FN];
+  // Dequantise in place, the fp32 value reusing the int32 accumulator's
+  // registers (the f32 and i32 32x32 MFMAs share one register layout).  With
+  // whole tiles the bias joins here, fl32(fl32(acc * SCA) * SCB / 127^2 +
+  // bias), four consecutive row scales come in one 16-byte load, and the
+  // stores below take two outputs each (N even keeps them aligned); otherwise
+  // every access is bounds-checked and the bias is added at the end, which
+  // keeps the checked path within the register budget.
+  float sb[FN], bv[FN];
 #pragma unroll
   for (int j = 0; j < FN; ++j) {
     const int64_t col = cbase + j * 32;
     sb[j] = (col < N) ? SCB[col] * (1.0f / 16129.0f) : 0.0f;
+    if constexpr (FL) bv[j] = (bias != nullptr) ? to_f32<DT>(bias[col]) : 0.0f;
   }
+  if constexpr (FL) {
 #pragma unroll
-  for (int i = 0; i < FM; ++i) {
+    for (int i = 0; i < FM; ++i) {
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int64_t row = rbase + i * 32 + 8 * (r >> 2) + (r & 3);
-      const float sa = (row < T) ? SCA[row] : 0.0f;
+      for (int q = 0; q < 4; ++q) {  // rows 8 q + 4 (lane / 32) + 0..3 of this 32-row strip
+        const v4f sa4 = *reinterpret_cast<const v4f*>(SCA + rbase + i * 32 + 8 * q);
 #pragma unroll
-      for (int j = 0; j < FN; ++j)
-        acc[i][j][r] = __float_as_int((float)acc[i][j][r] * (sa * sb[j]));
+        for (int e = 0; e < 4; ++e)
+#pragma unroll
+          for (int j = 0; j < FN; ++j)
+            acc[i][j][4 * q + e] =
+                __float_as_int(__builtin_fmaf((float)acc[i][j][4 * q + e] * sa4[e], sb[j], bv[j]));
+      }
+      __builtin_amdgcn_sched_barrier(0);  // one strip's scales in flight at a time
     }
-    __builtin_amdgcn_sched_barrier(0);  // keep the per-row loads of one strip at a time
+  } else {
+#pragma unroll
+    for (int i = 0; i < FM; ++i) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int64_t row = rbase + i * 32 + 8 * (r >> 2) + (r & 3);
+        const float sa = (row < T) ? SCA[row] : 0.0f;
+#pragma unroll
+        for (int j = 0; j < FN; ++j)
+          acc[i][j][r] = __float_as_int((float)acc[i][j][r] * (sa * sb[j]));
+      }
+      __builtin_amdgcn_sched_barrier(0);  // keep the per-row loads of one strip at a time
+    }
   }
 
   // 16-bit outlier product, 32 outlier columns per step.
@@ -588,25 +628,54 @@ __global__ __launch_bounds__(64 * WGM * WGN) void linear_tile_kernel(
     }
   }
 
-  // bias, one rounding to the output dtype, store.
-  float bv[FN];
+  // One rounding to the output dtype, store.
+  if constexpr (FL) {
+    // Rows R and R + 1 of a lane's column convert to one packed dword; lanes
+    // 2c and 2c + 1 trade halves of it, so the even lane holds row R of
+    // columns 2c, 2c + 1 and the odd lane row R + 1 of the same two columns:
+    // one 4-byte store per two values.  Row offsets are uniform, so the
+    // stores take a scalar base and one per-lane offset.
+    const int odd = lane & 1;
+    const uint32_t sel = odd ? 0x03020706u : 0x05040100u;  // odd: (nb.hi, own.hi), even: (own.lo, nb.lo)
+    const uint32_t loff = (uint32_t)(((4 * (lane >> 5) + odd) * N + (lane & 31) - odd) * 2);
+    const int swm = __builtin_amdgcn_readfirstlane(wm), swn = __builtin_amdgcn_readfirstlane(wn);
+    char* const ubase = reinterpret_cast<char*>(out + (m0 + swm * WM) * N + n0 + swn * WN);
 #pragma unroll
-  for (int j = 0; j < FN; ++j) {
-    const int64_t col = cbase + j * 32;
-    bv[j] = (bias != nullptr && col < N) ? to_f32<DT>(bias[col]) : 0.0f;
-  }
+    for (int i = 0; i < FM; ++i) {
 #pragma unroll
-  for (int i = 0; i < FM; ++i) {
+      for (int q = 0; q < 4; ++q) {
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int64_t row = rbase + i * 32 + 8 * (r >> 2) + (r & 3);
-      if (row >= T) continue;
-      uint16_t* orow = out + row * N + cbase;
+        for (int p = 0; p < 2; ++p) {
+          char* const rowp = ubase + (int64_t)(i * 32 + 8 * q + 2 * p) * N * 2;
 #pragma unroll
-      for (int j = 0; j < FN; ++j)
-        if (cbase + j * 32 < N) orow[j * 32] = from_f32<DT>(__int_as_float(acc[i][j][r]) + bv[j]);
+          for (int j = 0; j < FN; ++j) {
+            const uint32_t pk = pack2<DT>(__int_as_float(acc[i][j][4 * q + 2 * p]),
+                                          __int_as_float(acc[i][j][4 * q + 2 * p + 1]));
+            const uint32_t nb = (uint32_t)__builtin_amdgcn_mov_dpp((int)pk, 0xB1, 0xF, 0xF, false);  // lane ^ 1
+            *reinterpret_cast<uint32_t*>(rowp + j * 64 + loff) = __builtin_amdgcn_perm(nb, pk, sel);
+          }
+        }
+      }
     }
-    __builtin_amdgcn_sched_barrier(0);
+  } else {
+#pragma unroll
+    for (int j = 0; j < FN; ++j) {
+      const int64_t col = cbase + j * 32;
+      bv[j] = (bias != nullptr && col < N) ? to_f32<DT>(bias[col]) : 0.0f;
+    }
+#pragma unroll
+    for (int i = 0; i < FM; ++i) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int64_t row = rbase + i * 32 + 8 * (r >> 2) + (r & 3);
+        if (row >= T) continue;
+        uint16_t* orow = out + row * N + cbase;
+#pragma unroll
+        for (int j = 0; j < FN; ++j)
+          if (cbase + j * 32 < N) orow[j * 32] = from_f32<DT>(__int_as_float(acc[i][j][r]) + bv[j]);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
   }
 }
 
@@ -711,15 +780,19 @@ template <int DT, int BM, int BN, int BK, int WGM, int WGN, int GM = 8, int DL =
 static hipError_t launch_tile(const LinearArgs& a, hipStream_t s) {
   const int tiles_m = (int)((a.T + BM - 1) / BM), tiles_n = (int)((a.N + BN - 1) / BN);
   const int nb = tiles_m * tiles_n;
-  decltype(&linear_tile_kernel<DT, BM, BN, 0, BK, WGM, WGN, GM, DL>) k;
+  // whole tiles only: the epilogue without bounds checks
+  const bool full = (a.T % BM) == 0 && (a.N % BN) == 0 && (a.N % 2) == 0;
+  decltype(&linear_tile_kernel<DT, BM, BN, 0, BK, WGM, WGN, GM, DL, 0>) k;
   if constexpr (DL != 0) {  // direct-load configurations need K a multiple of the step
     if ((a.K % BK) != 0) return hipErrorInvalidValue;
     if (DL == 2 && (a.K / BK) % 2 != 0) return hipErrorInvalidValue;  // the 2-slot loop runs steps in pairs
-    k = linear_tile_kernel<DT, BM, BN, 0, BK, WGM, WGN, GM, DL>;
+    k = full ? linear_tile_kernel<DT, BM, BN, 0, BK, WGM, WGN, GM, DL, 1>
+             : linear_tile_kernel<DT, BM, BN, 0, BK, WGM, WGN, GM, DL, 0>;
   } else {
-    k = (a.K % BK) == 0 ? linear_tile_kernel<DT, BM, BN, 0, BK, WGM, WGN, GM, 0>
-        : (a.K % 16) == 0 ? linear_tile_kernel<DT, BM, BN, 1, BK, WGM, WGN, GM, 0>
-                          : linear_tile_kernel<DT, BM, BN, 2, BK, WGM, WGN, GM, 0>;
+    k = (a.K % BK) == 0 ? (full ? linear_tile_kernel<DT, BM, BN, 0, BK, WGM, WGN, GM, 0, 1>
+                                : linear_tile_kernel<DT, BM, BN, 0, BK, WGM, WGN, GM, 0, 0>)
+        : (a.K % 16) == 0 ? linear_tile_kernel<DT, BM, BN, 1, BK, WGM, WGN, GM, 0, 0>
+                          : linear_tile_kernel<DT, BM, BN, 2, BK, WGM, WGN, GM, 0, 0>;
   }
   k<<<dim3(nb), dim3(64 * WGM * WGN), 0, s>>>(a.CA, a.CB, a.SCA, a.SCB, static_cast<const uint16_t*>(a.bias),
                                    static_cast<const uint16_t*>(a.xo), a.idx, a.n_idx,
