@@ -8,7 +8,10 @@
 // the weight recovered as (CB * SCB) / 127 (section "Integration into
 // transformers") and the two results are summed.
 //
-// Two kernels:
+// Three kernels:
+//   * persistent kernel (T, N, K multiples of 256): the 256 x 256 2-slot
+//     tile loop below, one workgroup per compute unit walking its tiles,
+//     the next tile's first steps loaded during the current tile's epilogue.
 //   * tile kernel: BM x BN output tile per workgroup of WGM x WGN waves.
 //     Large problems (T, N >= 512): 256 x 256 on 4 x 2 waves (two per SIMD),
 //     K straight from memory into LDS with global_load_lds: 128-byte steps
@@ -119,6 +122,295 @@ __device__ __forceinline__ void interleave_mfma() {
   }
 }
 
+// The tile epilogue: int32 tile (copied to acc_out when asked) -> fp32
+// dequantised -> plus the 16-bit outlier product -> one rounding -> out.
+// ring_a/ring_b are the LDS buffers: with PF = 0 the outlier operands are
+// staged there (the ring slots of a direct-load kernel; the first buffer for
+// weights gathered from CB).  PF = 1 (whole tiles, every chunk's recovered
+// weights in scratch) loads them straight into registers and leaves LDS
+// alone, so the caller's loads of its next tile can be in flight; its
+// before_store() runs once the last value the epilogue waits for has
+// arrived, before the stores.
+template <int DT, int BM, int BN, int WGM, int WGN, int DL, int FL, int PF, class F>
+__device__ __forceinline__ void tile_epilogue(
+    v16i (&acc)[BM / WGM / 32][BN / WGN / 32], int64_t m0, int64_t n0, int T, int N, int K,
+    const float* __restrict__ SCA, const float* __restrict__ SCB, const uint16_t* __restrict__ bias,
+    const uint16_t* __restrict__ xo, const int32_t* __restrict__ idx, int n_idx, const int8_t* __restrict__ CB,
+    const uint16_t* __restrict__ wo, int wo_chunks, uint16_t* __restrict__ out, int32_t* __restrict__ acc_out,
+    int8_t* const (&ra)[4], int8_t* const (&rb)[4], F&& before_store) {
+  static_assert(!PF || FL, "register-staged outlier operands need whole tiles");
+  constexpr int NT = 64 * WGM * WGN;
+  constexpr int WM = BM / WGM, WN = BN / WGN;
+  constexpr int FM = WM / 32, FN = WN / 32;
+  // the thread index through an empty asm: nothing derived from it is
+  // hoisted out of a caller's tile loop to sit in registers through the
+  // K loop
+  int tid = threadIdx.x;
+  asm volatile("" : "+v"(tid));
+  const int lane = tid & 63, wid = tid >> 6;
+  const int wm = wid / WGN, wn = wid % WGN;
+  int8_t* const ep_a = ra[0];
+  int8_t* const ep_b = rb[0];
+  // ---- epilogue.  32x32 accumulator layout: lane holds column (lane & 31),
+  // register r holds row 8 * (r / 4) + 4 * (lane / 32) + r % 4.
+  const int64_t rbase = m0 + wm * WM + 4 * (lane >> 5);
+  const int64_t cbase = n0 + wn * WN + (lane & 31);
+  if (acc_out != nullptr) {
+#pragma unroll
+    for (int i = 0; i < FM; ++i) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int64_t row = rbase + i * 32 + 8 * (r >> 2) + (r & 3);
+        if (row >= T) continue;
+        int32_t* arow = acc_out + row * N + cbase;
+#pragma unroll
+        for (int j = 0; j < FN; ++j)
+          if (cbase + j * 32 < N) arow[j * 32] = acc[i][j][r];
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  }
+  // Dequantise in place, the fp32 value reusing the int32 accumulator's
+  // registers (the f32 and i32 32x32 MFMAs share one register layout).  With
+  // whole tiles the bias joins here, fl32(fl32(acc * SCA) * SCB / 127^2 +
+  // bias), four consecutive row scales come in one 16-byte load, and the
+  // stores below take two outputs each (N even keeps them aligned); otherwise
+  // every access is bounds-checked and the bias is added at the end, which
+  // keeps the checked path within the register budget.
+  float sb[FN], bv[FN];
+#pragma unroll
+  for (int j = 0; j < FN; ++j) {
+    const int64_t col = cbase + j * 32;
+    sb[j] = (col < N) ? SCB[col] * (1.0f / 16129.0f) : 0.0f;
+    if constexpr (FL) bv[j] = (bias != nullptr) ? to_f32<DT>(bias[col]) : 0.0f;
+  }
+  if constexpr (FL) {
+#pragma unroll
+    for (int i = 0; i < FM; ++i) {
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {  // rows 8 q + 4 (lane / 32) + 0..3 of this 32-row strip
+        const v4f sa4 = *reinterpret_cast<const v4f*>(SCA + rbase + i * 32 + 8 * q);
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+#pragma unroll
+          for (int j = 0; j < FN; ++j)
+            acc[i][j][4 * q + e] =
+                __float_as_int(__builtin_fmaf((float)acc[i][j][4 * q + e] * sa4[e], sb[j], bv[j]));
+      }
+      __builtin_amdgcn_sched_barrier(0);  // one strip's scales in flight at a time
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < FM; ++i) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int64_t row = rbase + i * 32 + 8 * (r >> 2) + (r & 3);
+        const float sa = (row < T) ? SCA[row] : 0.0f;
+#pragma unroll
+        for (int j = 0; j < FN; ++j)
+          acc[i][j][r] = __float_as_int((float)acc[i][j][r] * (sa * sb[j]));
+      }
+      __builtin_amdgcn_sched_barrier(0);  // keep the per-row loads of one strip at a time
+    }
+  }
+
+  // 16-bit outlier product, 32 outlier columns per step.
+  const int n_chunks = (n_idx + 31) >> 5;
+  if constexpr (PF) {
+    // operands straight from the chunk-major 64-byte rows of Xo and of the
+    // recovered weights: lane (row l % 32) takes the 16-byte piece
+    // 2 s + l / 32 for sub-step s, the MFMA operand layout
+    for (int ch = 0; ch < n_chunks; ++ch) {
+      u32x4 a[2][FM], b[2][FN];
+#pragma unroll
+      for (int s = 0; s < 2; ++s) {
+        const int c = 2 * s + (lane >> 5);
+#pragma unroll
+        for (int i = 0; i < FM; ++i)
+          a[s][i] = *reinterpret_cast<const u32x4*>(
+              xo + (((int64_t)ch * T + m0 + wm * WM + i * 32 + (lane & 31)) * 32 + c * 8));
+#pragma unroll
+        for (int j = 0; j < FN; ++j)
+          b[s][j] = *reinterpret_cast<const u32x4*>(
+              wo + (((int64_t)ch * N + n0 + wn * WN + j * 32 + (lane & 31)) * 32 + c * 8));
+      }
+#pragma unroll
+      for (int s = 0; s < 2; ++s)
+#pragma unroll
+        for (int i = 0; i < FM; ++i)
+#pragma unroll
+          for (int j = 0; j < FN; ++j)
+            acc[i][j] = __builtin_bit_cast(v16i, mfma16<DT>(a[s][i], b[s][j], __builtin_bit_cast(v16f, acc[i][j])));
+    }
+  } else {
+  int ch_done = 0;
+  if constexpr (DL != 0) {
+    // With the recovered weights in scratch, both operands are chunk-major
+    // 64-byte rows: the chunks stream through the same LDS ring as the int8
+    // steps (direct loads, DL slots), into the dequantised fp32 registers.
+    if (n_chunks > 0 && n_chunks <= wo_chunks) {
+      constexpr int NW = WGM * WGN;
+      constexpr int IA = BM / 16 / NW, IB = BN / 16 / NW;  // 1 KiB loads per wave per chunk (16 rows each)
+      static_assert(IA * 16 * NW == BM && IB * 16 * NW == BN, "tile rows must split evenly over the waves");
+      const int8_t* xa[IA];
+      const int8_t* wb[IB];
+#pragma unroll
+      for (int j = 0; j < IA; ++j) {
+        const int r = (wid * IA + j) * 16 + (lane >> 2);
+        const int64_t row = m0 + r < T ? m0 + r : (int64_t)T - 1;
+        xa[j] = reinterpret_cast<const int8_t*>(xo) + row * 64 + (((lane & 3) ^ ((r >> 2) & 3)) << 4);
+      }
+#pragma unroll
+      for (int j = 0; j < IB; ++j) {
+        const int r = (wid * IB + j) * 16 + (lane >> 2);
+        const int64_t row = n0 + r < N ? n0 + r : (int64_t)N - 1;
+        wb[j] = reinterpret_cast<const int8_t*>(wo) + row * 64 + (((lane & 3) ^ ((r >> 2) & 3)) << 4);
+      }
+      auto issue16 = [&](int ch, int8_t* a_slot, int8_t* b_slot) {
+        const int c = ch < n_chunks ? ch : n_chunks - 1;
+        const int64_t oa = (int64_t)c * T * 64, ob = (int64_t)c * N * 64;
+#pragma unroll
+        for (int j = 0; j < IA; ++j) load_lds16(xa[j] + oa, a_slot + (wid * IA + j) * 1024);
+#pragma unroll
+        for (int j = 0; j < IB; ++j) load_lds16(wb[j] + ob, b_slot + (wid * IB + j) * 1024);
+      };
+      __syncthreads();  // everyone is done with the ring's int8 contents
+#pragma unroll
+      for (int st = 0; st < DL - 1; ++st) issue16(st, ra[st], rb[st]);
+      for (int cg = 0; cg < n_chunks; cg += DL) {
+#pragma unroll
+        for (int i = 0; i < DL; ++i) {
+          wait_vmcnt<(DL - 2) * (IA + IB)>();
+          __builtin_amdgcn_s_barrier();
+          __builtin_amdgcn_sched_barrier(0);
+          issue16(cg + i + DL - 1, ra[(i + DL - 1) % DL], rb[(i + DL - 1) % DL]);
+          if (cg + i < n_chunks) {
+#pragma unroll
+            for (int s2 = 0; s2 < 2; ++s2) {
+              const int c = 2 * s2 + (lane >> 5);
+              u32x4 a[FM], b[FN];
+#pragma unroll
+              for (int ii = 0; ii < FM; ++ii)
+                a[ii] = *reinterpret_cast<const u32x4*>(ra[i] + tile_off<64>(wm * WM + ii * 32 + (lane & 31), c));
+#pragma unroll
+              for (int jj = 0; jj < FN; ++jj)
+                b[jj] = *reinterpret_cast<const u32x4*>(rb[i] + tile_off<64>(wn * WN + jj * 32 + (lane & 31), c));
+#pragma unroll
+              for (int ii = 0; ii < FM; ++ii)
+#pragma unroll
+                for (int jj = 0; jj < FN; ++jj)
+                  acc[ii][jj] = __builtin_bit_cast(v16i, mfma16<DT>(a[ii], b[jj], __builtin_bit_cast(v16f, acc[ii][jj])));
+            }
+          }
+          __builtin_amdgcn_sched_barrier(0);
+        }
+      }
+      wait_vmcnt<0>();
+      ch_done = n_chunks;
+    }
+  }
+  int8_t* oA = ep_a;  // [BM][32] 16-bit values, 64-byte rows
+  int8_t* oB = ep_b;  // [BN][32]
+  for (int ch = ch_done; ch < n_chunks; ++ch) {
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < BM * 4 / NT; ++i) {
+      const int q = tid + NT * i, r = q >> 2, c = q & 3;
+      u32x4 v = {0u, 0u, 0u, 0u};
+      if (m0 + r < T) v = *reinterpret_cast<const u32x4*>(xo + (((int64_t)ch * T + m0 + r) * 32 + c * 8));
+      *reinterpret_cast<u32x4*>(oA + lds_off(r, c)) = v;
+    }
+    if (ch < wo_chunks) {  // recovered weights precomputed once per call: contiguous rows
+#pragma unroll
+      for (int i = 0; i < BN * 4 / NT; ++i) {
+        const int q = tid + NT * i, r = q >> 2, c = q & 3;
+        u32x4 v = {0u, 0u, 0u, 0u};
+        if (n0 + r < N) v = *reinterpret_cast<const u32x4*>(wo + (((int64_t)ch * N + n0 + r) * 32 + c * 8));
+        *reinterpret_cast<u32x4*>(oB + lds_off(r, c)) = v;
+      }
+    } else {  // gathered here
+      const int j = tid & 31;
+      const int p = ch * 32 + j;
+      const bool valid = p < n_idx;
+      const int64_t col = valid ? idx[p] : 0;
+      for (int rr = tid >> 5; rr < BN; rr += NT / 32) {
+        const int64_t gn = n0 + rr;
+        uint16_t w = 0;
+        if (valid && gn < N) w = recover_w<DT>(CB[gn * K + col], SCB[gn]);
+        *reinterpret_cast<uint16_t*>(oB + lds_off(rr, j >> 3) + (j & 7) * 2) = w;
+      }
+    }
+    __syncthreads();
+#pragma unroll
+    for (int s = 0; s < 2; ++s) {
+      const int c = 2 * s + (lane >> 5);
+      u32x4 a[FM], b[FN];
+#pragma unroll
+      for (int i = 0; i < FM; ++i) a[i] = *reinterpret_cast<const u32x4*>(oA + lds_off(wm * WM + i * 32 + (lane & 31), c));
+#pragma unroll
+      for (int j = 0; j < FN; ++j) b[j] = *reinterpret_cast<const u32x4*>(oB + lds_off(wn * WN + j * 32 + (lane & 31), c));
+#pragma unroll
+      for (int i = 0; i < FM; ++i)
+#pragma unroll
+        for (int j = 0; j < FN; ++j)
+          acc[i][j] = __builtin_bit_cast(v16i, mfma16<DT>(a[i], b[j], __builtin_bit_cast(v16f, acc[i][j])));
+    }
+  }
+  }  // PF
+
+  before_store();
+
+  // One rounding to the output dtype, store.
+  if constexpr (FL) {
+    // Rows R and R + 1 of a lane's column convert to one packed dword; lanes
+    // 2c and 2c + 1 trade halves of it, so the even lane holds row R of
+    // columns 2c, 2c + 1 and the odd lane row R + 1 of the same two columns:
+    // one 4-byte store per two values.  Row offsets are uniform, so the
+    // stores take a scalar base and one per-lane offset.
+    const int odd = lane & 1;
+    const uint32_t sel = odd ? 0x03020706u : 0x05040100u;  // odd: (nb.hi, own.hi), even: (own.lo, nb.lo)
+    const uint32_t loff = (uint32_t)(((4 * (lane >> 5) + odd) * N + (lane & 31) - odd) * 2);
+    const int swm = __builtin_amdgcn_readfirstlane(wm), swn = __builtin_amdgcn_readfirstlane(wn);
+    char* const ubase = reinterpret_cast<char*>(out + (m0 + swm * WM) * N + n0 + swn * WN);
+#pragma unroll
+    for (int i = 0; i < FM; ++i) {
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+#pragma unroll
+        for (int p = 0; p < 2; ++p) {
+          char* const rowp = ubase + (int64_t)(i * 32 + 8 * q + 2 * p) * N * 2;
+#pragma unroll
+          for (int j = 0; j < FN; ++j) {
+            const uint32_t pk = pack2<DT>(__int_as_float(acc[i][j][4 * q + 2 * p]),
+                                          __int_as_float(acc[i][j][4 * q + 2 * p + 1]));
+            const uint32_t nb = (uint32_t)__builtin_amdgcn_mov_dpp((int)pk, 0xB1, 0xF, 0xF, false);  // lane ^ 1
+            *reinterpret_cast<uint32_t*>(rowp + j * 64 + loff) = __builtin_amdgcn_perm(nb, pk, sel);
+          }
+        }
+      }
+    }
+  } else {
+#pragma unroll
+    for (int j = 0; j < FN; ++j) {
+      const int64_t col = cbase + j * 32;
+      bv[j] = (bias != nullptr && col < N) ? to_f32<DT>(bias[col]) : 0.0f;
+    }
+#pragma unroll
+    for (int i = 0; i < FM; ++i) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int64_t row = rbase + i * 32 + 8 * (r >> 2) + (r & 3);
+        if (row >= T) continue;
+        uint16_t* orow = out + row * N + cbase;
+#pragma unroll
+        for (int j = 0; j < FN; ++j)
+          if (cbase + j * 32 < N) orow[j * 32] = from_f32<DT>(__int_as_float(acc[i][j][r]) + bv[j]);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  }
+}
+
 // DL = 0: global loads staged through registers, LDS double buffered (any K).
 // DL = 2 (K a multiple of 2 BK): loads go straight from global memory into two
 // LDS slots, two steps in flight, steps run in pairs.
@@ -151,9 +443,6 @@ __global__ __launch_bounds__(64 * WGM * WGN) void linear_tile_kernel(
   __shared__ __attribute__((aligned(16))) int8_t dB0[RB], dB1[RB], dB2[DL >= 3 ? RB : 1], dB3[DL >= 4 ? RB : 1];
   int8_t (*sA)[BM * BK] = reinterpret_cast<int8_t (*)[BM * BK]>(sA_);
   int8_t (*sB)[BN * BK] = reinterpret_cast<int8_t (*)[BN * BK]>(sB_);
-  // the epilogue stages the outlier columns in the first buffer
-  int8_t* const ep_a = DL ? dA0 : sA_;
-  int8_t* const ep_b = DL ? dB0 : sB_;
 
   const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
   const int wm = wid / WGN, wn = wid % WGN;
@@ -447,236 +736,189 @@ __global__ __launch_bounds__(64 * WGM * WGN) void linear_tile_kernel(
     __syncthreads();
   }
 
-  // ---- epilogue.  32x32 accumulator layout: lane holds column (lane & 31),
-  // register r holds row 8 * (r / 4) + 4 * (lane / 32) + r % 4.
-  const int64_t rbase = m0 + wm * WM + 4 * (lane >> 5);
-  const int64_t cbase = n0 + wn * WN + (lane & 31);
-  if (acc_out != nullptr) {
+  int8_t* const ring_a[4] = {DL ? dA0 : sA_, dA1, dA2, dA3};
+  int8_t* const ring_b[4] = {DL ? dB0 : sB_, dB1, dB2, dB3};
+  tile_epilogue<DT, BM, BN, WGM, WGN, DL, FL, 0>(acc, m0, n0, T, N, K, SCA, SCB, bias, xo, idx, n_idx, CB, wo,
+                                                 wo_chunks, out, acc_out, ring_a, ring_b, [] {});
+}
+
+// ----------------------------------------------------------- persistent ----
+// 256 x 256 tiles, 128-byte steps in the 2-slot direct-load ring, whole tiles
+// only (T % 256 == 0, N % 256 == 0, K % 256 == 0).  One workgroup per compute
+// unit walks tiles blockIdx.x, blockIdx.x + gridDim.x, ...; with a multiple
+// of 8 workgroups each keeps to one XCD, and at any moment an XCD works on
+// neighbouring tiles, as a one-tile-per-workgroup grid would.  When at most
+// PF_CHUNKS outlier chunks come with recovered weights in scratch, the last
+// step of a tile loads the next tile's first step into the free ring slot
+// and the epilogue keeps out of LDS (outlier operands straight into
+// registers), so the next tile's first step arrives during the epilogue and
+// its second while the stores drain.  Otherwise each tile runs on its own,
+// its outlier columns staged through LDS.
+constexpr int PF_CHUNKS = 4;
+
+template <int DT, int PF>
+__device__ __forceinline__ void persist_tiles(
+    const int8_t* __restrict__ CA, const int8_t* __restrict__ CB, const float* __restrict__ SCA,
+    const float* __restrict__ SCB, const uint16_t* __restrict__ bias, const uint16_t* __restrict__ xo,
+    const int32_t* __restrict__ idx, int n_idx, uint16_t* __restrict__ out, int32_t* __restrict__ acc_out,
+    int T, int N, int K, int tiles_m, int tiles_n, const uint16_t* __restrict__ wo, int wo_chunks,
+    int8_t* dA0, int8_t* dA1, int8_t* dB0, int8_t* dB1) {
+  constexpr int BM = 256, BN = 256, BK = 128, WGM = 4, WGN = 2, GM = 4;
+  constexpr int NW = WGM * WGN, WM = BM / WGM, WN = BN / WGN, FM = WM / 32, FN = WN / 32;
+  constexpr int CPR = BK / 16, SS = BK / 32, RPI = 1024 / BK;
+  constexpr int IA = BM / RPI / NW, IB = BN / RPI / NW;
+  constexpr int NFR = FM + FN, NLD = IA + IB;
+  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+  const int wm = wid / WGN, wn = wid % WGN;
+  const int swid = __builtin_amdgcn_readfirstlane(wid);
+  const int nb = tiles_m * tiles_n, nk = K / BK;
+  const bool int8_part = n_idx < K;  // otherwise CA is all zeros: nothing to multiply
+  // the tile's rows in the ring's swizzled order; the same for every tile
+  uint32_t oa[IA], ob[IB];
 #pragma unroll
-    for (int i = 0; i < FM; ++i) {
+  for (int j = 0; j < IA; ++j) {
+    const int r = (wid * IA + j) * RPI + lane / CPR;
+    oa[j] = (uint32_t)r * (uint32_t)K + (uint32_t)(((lane % CPR) ^ ((r >> 1) & 7)) << 4);
+  }
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int64_t row = rbase + i * 32 + 8 * (r >> 2) + (r & 3);
-        if (row >= T) continue;
-        int32_t* arow = acc_out + row * N + cbase;
+  for (int j = 0; j < IB; ++j) {
+    const int r = (wid * IB + j) * RPI + lane / CPR;
+    ob[j] = (uint32_t)r * (uint32_t)K + (uint32_t)(((lane % CPR) ^ ((r >> 1) & 7)) << 4);
+  }
+  auto issue = [&](const int8_t* ba, const int8_t* bb, int8_t* a_slot, int8_t* b_slot) {
+    // the step's base stays a scalar pair (load = scalar base + 32-bit lane
+    // offset), rather than being folded into 64-bit per-lane addresses
+    asm volatile("" : "+s"(ba), "+s"(bb));
 #pragma unroll
-        for (int j = 0; j < FN; ++j)
-          if (cbase + j * 32 < N) arow[j * 32] = acc[i][j][r];
+    for (int j = 0; j < IA; ++j) load_lds16(ba + oa[j], a_slot + (swid * IA + j) * 1024);
+#pragma unroll
+    for (int j = 0; j < IB; ++j) load_lds16(bb + ob[j], b_slot + (swid * IB + j) * 1024);
+  };
+  v4i fa0[FM], fb0[FN], fa1[FM], fb1[FN];
+  auto frags = [&](const int8_t* a_slot, const int8_t* b_slot, int s, v4i (&fa)[FM], v4i (&fb)[FN]) {
+    const int c = 2 * s + (lane >> 5);
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+      fa[i] = *reinterpret_cast<const v4i*>(a_slot + tile_off<BK>(wm * WM + i * 32 + (lane & 31), c));
+#pragma unroll
+    for (int j = 0; j < FN; ++j)
+      fb[j] = *reinterpret_cast<const v4i*>(b_slot + tile_off<BK>(wn * WN + j * 32 + (lane & 31), c));
+  };
+  v16i acc[FM][FN];
+  auto mfmas = [&](const v4i (&fa)[FM], const v4i (&fb)[FN]) {
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+      for (int j = 0; j < FN; ++j)
+        acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(fa[i], fb[j], acc[i][j], 0, 0, 0);
+  };
+  // Sub-steps 0 .. SS - 2 of the step in slot (a_cur, b_cur), whose sub-step
+  // 0 operands are already in set 0; then the step's one barrier (every
+  // wave's loads of the next step have landed, nobody reads this slot any
+  // more), and the last sub-step's MFMAs behind it.
+  auto substeps = [&](const int8_t* a_cur, const int8_t* b_cur) {
+#pragma unroll
+    for (int s = 0; s + 1 < SS; ++s) {
+      if (s % 2 == 0) {
+        frags(a_cur, b_cur, s + 1, fa1, fb1);
+        mfmas(fa0, fb0);
+      } else {
+        frags(a_cur, b_cur, s + 1, fa0, fb0);
+        mfmas(fa1, fb1);
       }
+      interleave_mfma<FM * FN, NFR, 0>();
       __builtin_amdgcn_sched_barrier(0);
     }
-  }
-  // Dequantise in place, the fp32 value reusing the int32 accumulator's
-  // registers (the f32 and i32 32x32 MFMAs share one register layout).  With
-  // whole tiles the bias joins here, fl32(fl32(acc * SCA) * SCB / 127^2 +
-  // bias), four consecutive row scales come in one 16-byte load, and the
-  // stores below take two outputs each (N even keeps them aligned); otherwise
-  // every access is bounds-checked and the bias is added at the end, which
-  // keeps the checked path within the register budget.
-  float sb[FN], bv[FN];
-#pragma unroll
-  for (int j = 0; j < FN; ++j) {
-    const int64_t col = cbase + j * 32;
-    sb[j] = (col < N) ? SCB[col] * (1.0f / 16129.0f) : 0.0f;
-    if constexpr (FL) bv[j] = (bias != nullptr) ? to_f32<DT>(bias[col]) : 0.0f;
-  }
-  if constexpr (FL) {
-#pragma unroll
-    for (int i = 0; i < FM; ++i) {
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {  // rows 8 q + 4 (lane / 32) + 0..3 of this 32-row strip
-        const v4f sa4 = *reinterpret_cast<const v4f*>(SCA + rbase + i * 32 + 8 * q);
-#pragma unroll
-        for (int e = 0; e < 4; ++e)
-#pragma unroll
-          for (int j = 0; j < FN; ++j)
-            acc[i][j][4 * q + e] =
-                __float_as_int(__builtin_fmaf((float)acc[i][j][4 * q + e] * sa4[e], sb[j], bv[j]));
-      }
-      __builtin_amdgcn_sched_barrier(0);  // one strip's scales in flight at a time
-    }
-  } else {
-#pragma unroll
-    for (int i = 0; i < FM; ++i) {
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int64_t row = rbase + i * 32 + 8 * (r >> 2) + (r & 3);
-        const float sa = (row < T) ? SCA[row] : 0.0f;
-#pragma unroll
-        for (int j = 0; j < FN; ++j)
-          acc[i][j][r] = __float_as_int((float)acc[i][j][r] * (sa * sb[j]));
-      }
-      __builtin_amdgcn_sched_barrier(0);  // keep the per-row loads of one strip at a time
-    }
-  }
+    __builtin_amdgcn_s_waitcnt(0);
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_sched_barrier(0);
+  };
+  int8_t* const ring_a[4] = {dA0, dA1, dA1, dA1};
+  int8_t* const ring_b[4] = {dB0, dB1, dB1, dB1};
 
-  // 16-bit outlier product, 32 outlier columns per step.
+  bool first = true;
+  for (int v = blockIdx.x; v < nb; v += gridDim.x) {
+    const int vn = v + gridDim.x;
+    const bool more = vn < nb;
+    int tm, tn;
+    tile_coords<GM>(v, tiles_m, tiles_n, tm, tn);
+    const int64_t m0 = (int64_t)tm * BM, n0 = (int64_t)tn * BN;
+    const int8_t* const ta = CA + m0 * K;
+    const int8_t* const tb = CB + n0 * K;
+    int tmn = tm, tnn = tn;
+    if (more) tile_coords<GM>(vn, tiles_m, tiles_n, tmn, tnn);
+    const int8_t* const tan = CA + (int64_t)tmn * BM * K;  // the next tile's rows
+    const int8_t* const tbn = CB + (int64_t)tnn * BN * K;
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+      for (int j = 0; j < FN; ++j) acc[i][j] = (v16i){0};
+    if (int8_part) {
+      if (!PF || first) {
+        if (!first) __syncthreads();  // the previous epilogue is done with LDS
+        issue(ta, tb, dA0, dB0);
+        issue(ta + BK, tb + BK, dA1, dB1);
+        wait_vmcnt<NLD>();
+        __builtin_amdgcn_s_barrier();
+      }
+      // (PF, later tiles: step 0 is in slot 0 since the previous tile's last
+      // barrier, step 1 on its way since its epilogue)
+      frags(dA0, dB0, 0, fa0, fb0);
+      for (int kg = 0; kg + 2 < nk; kg += 2) {
+        substeps(dA0, dB0);
+        issue(ta + (int64_t)(kg + 2) * BK, tb + (int64_t)(kg + 2) * BK, dA0, dB0);
+        frags(dA1, dB1, 0, fa0, fb0);
+        mfmas(fa1, fb1);
+        interleave_mfma<FM * FN, NFR, NLD>();
+        __builtin_amdgcn_sched_barrier(0);
+        substeps(dA1, dB1);
+        issue(ta + (int64_t)(kg + 3) * BK, tb + (int64_t)(kg + 3) * BK, dA1, dB1);
+        frags(dA0, dB0, 0, fa0, fb0);
+        mfmas(fa1, fb1);
+        interleave_mfma<FM * FN, NFR, NLD>();
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      // the last two steps: slot 0 then takes the next tile's first step
+      substeps(dA0, dB0);
+      if (PF && more) issue(tan, tbn, dA0, dB0);
+      frags(dA1, dB1, 0, fa0, fb0);
+      mfmas(fa1, fb1);
+      interleave_mfma<FM * FN, NFR, 0>();
+      __builtin_amdgcn_sched_barrier(0);
+      substeps(dA1, dB1);
+      mfmas(fa1, fb1);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    if constexpr (!PF) __syncthreads();  // the epilogue may stage through LDS
+    tile_epilogue<DT, BM, BN, WGM, WGN, 2, 1, PF>(
+        acc, m0, n0, T, N, K, SCA, SCB, bias, xo, idx, n_idx, CB, wo, wo_chunks, out, acc_out, ring_a, ring_b,
+        [&] {
+          // the next tile's second step, once every wave is past the last
+          // barrier (nobody reads slot 1 any more)
+          if (PF && more && int8_part) issue(tan + BK, tbn + BK, dA1, dB1);
+        });
+    first = false;
+  }
+  wait_vmcnt<0>();  // no load into LDS outlives the workgroup
+}
+
+template <int DT>
+__global__ __launch_bounds__(512) void linear_persist_kernel(
+    const int8_t* __restrict__ CA, const int8_t* __restrict__ CB, const float* __restrict__ SCA,
+    const float* __restrict__ SCB, const uint16_t* __restrict__ bias, const uint16_t* __restrict__ xo,
+    const int32_t* __restrict__ idx, const int32_t* __restrict__ n_idx_p, uint16_t* __restrict__ out,
+    int32_t* __restrict__ acc_out, int T, int N, int K, int tiles_m, int tiles_n,
+    const uint16_t* __restrict__ wo, int wo_chunks) {
+  __shared__ __attribute__((aligned(16))) int8_t dA0[256 * 128], dA1[256 * 128];
+  __shared__ __attribute__((aligned(16))) int8_t dB0[256 * 128], dB1[256 * 128];
+  const int n_idx = *n_idx_p;
   const int n_chunks = (n_idx + 31) >> 5;
-  int ch_done = 0;
-  if constexpr (DL != 0) {
-    // With the recovered weights in scratch, both operands are chunk-major
-    // 64-byte rows: the chunks stream through the same LDS ring as the int8
-    // steps (direct loads, DL slots), into the dequantised fp32 registers.
-    if (n_chunks > 0 && n_chunks <= wo_chunks) {
-      constexpr int NW = WGM * WGN;
-      constexpr int IA = BM / 16 / NW, IB = BN / 16 / NW;  // 1 KiB loads per wave per chunk (16 rows each)
-      static_assert(IA * 16 * NW == BM && IB * 16 * NW == BN, "tile rows must split evenly over the waves");
-      const int8_t* xa[IA];
-      const int8_t* wb[IB];
-#pragma unroll
-      for (int j = 0; j < IA; ++j) {
-        const int r = (wid * IA + j) * 16 + (lane >> 2);
-        const int64_t row = m0 + r < T ? m0 + r : (int64_t)T - 1;
-        xa[j] = reinterpret_cast<const int8_t*>(xo) + row * 64 + (((lane & 3) ^ ((r >> 2) & 3)) << 4);
-      }
-#pragma unroll
-      for (int j = 0; j < IB; ++j) {
-        const int r = (wid * IB + j) * 16 + (lane >> 2);
-        const int64_t row = n0 + r < N ? n0 + r : (int64_t)N - 1;
-        wb[j] = reinterpret_cast<const int8_t*>(wo) + row * 64 + (((lane & 3) ^ ((r >> 2) & 3)) << 4);
-      }
-      auto issue16 = [&](int ch, int8_t* a_slot, int8_t* b_slot) {
-        const int c = ch < n_chunks ? ch : n_chunks - 1;
-        const int64_t oa = (int64_t)c * T * 64, ob = (int64_t)c * N * 64;
-#pragma unroll
-        for (int j = 0; j < IA; ++j) load_lds16(xa[j] + oa, a_slot + (wid * IA + j) * 1024);
-#pragma unroll
-        for (int j = 0; j < IB; ++j) load_lds16(wb[j] + ob, b_slot + (wid * IB + j) * 1024);
-      };
-      int8_t* const ra[4] = {dA0, dA1, dA2, dA3};
-      int8_t* const rb[4] = {dB0, dB1, dB2, dB3};
-      __syncthreads();  // everyone is done with the ring's int8 contents
-#pragma unroll
-      for (int st = 0; st < DL - 1; ++st) issue16(st, ra[st], rb[st]);
-      for (int cg = 0; cg < n_chunks; cg += DL) {
-#pragma unroll
-        for (int i = 0; i < DL; ++i) {
-          wait_vmcnt<(DL - 2) * (IA + IB)>();
-          __builtin_amdgcn_s_barrier();
-          __builtin_amdgcn_sched_barrier(0);
-          issue16(cg + i + DL - 1, ra[(i + DL - 1) % DL], rb[(i + DL - 1) % DL]);
-          if (cg + i < n_chunks) {
-#pragma unroll
-            for (int s2 = 0; s2 < 2; ++s2) {
-              const int c = 2 * s2 + (lane >> 5);
-              u32x4 a[FM], b[FN];
-#pragma unroll
-              for (int ii = 0; ii < FM; ++ii)
-                a[ii] = *reinterpret_cast<const u32x4*>(ra[i] + tile_off<64>(wm * WM + ii * 32 + (lane & 31), c));
-#pragma unroll
-              for (int jj = 0; jj < FN; ++jj)
-                b[jj] = *reinterpret_cast<const u32x4*>(rb[i] + tile_off<64>(wn * WN + jj * 32 + (lane & 31), c));
-#pragma unroll
-              for (int ii = 0; ii < FM; ++ii)
-#pragma unroll
-                for (int jj = 0; jj < FN; ++jj)
-                  acc[ii][jj] = __builtin_bit_cast(v16i, mfma16<DT>(a[ii], b[jj], __builtin_bit_cast(v16f, acc[ii][jj])));
-            }
-          }
-          __builtin_amdgcn_sched_barrier(0);
-        }
-      }
-      wait_vmcnt<0>();
-      ch_done = n_chunks;
-    }
-  }
-  int8_t* oA = ep_a;  // [BM][32] 16-bit values, 64-byte rows
-  int8_t* oB = ep_b;  // [BN][32]
-  for (int ch = ch_done; ch < n_chunks; ++ch) {
-    __syncthreads();
-#pragma unroll
-    for (int i = 0; i < BM * 4 / NT; ++i) {
-      const int q = tid + NT * i, r = q >> 2, c = q & 3;
-      u32x4 v = {0u, 0u, 0u, 0u};
-      if (m0 + r < T) v = *reinterpret_cast<const u32x4*>(xo + (((int64_t)ch * T + m0 + r) * 32 + c * 8));
-      *reinterpret_cast<u32x4*>(oA + lds_off(r, c)) = v;
-    }
-    if (ch < wo_chunks) {  // recovered weights precomputed once per call: contiguous rows
-#pragma unroll
-      for (int i = 0; i < BN * 4 / NT; ++i) {
-        const int q = tid + NT * i, r = q >> 2, c = q & 3;
-        u32x4 v = {0u, 0u, 0u, 0u};
-        if (n0 + r < N) v = *reinterpret_cast<const u32x4*>(wo + (((int64_t)ch * N + n0 + r) * 32 + c * 8));
-        *reinterpret_cast<u32x4*>(oB + lds_off(r, c)) = v;
-      }
-    } else {  // gathered here
-      const int j = tid & 31;
-      const int p = ch * 32 + j;
-      const bool valid = p < n_idx;
-      const int64_t col = valid ? idx[p] : 0;
-      for (int rr = tid >> 5; rr < BN; rr += NT / 32) {
-        const int64_t gn = n0 + rr;
-        uint16_t w = 0;
-        if (valid && gn < N) w = recover_w<DT>(CB[gn * K + col], SCB[gn]);
-        *reinterpret_cast<uint16_t*>(oB + lds_off(rr, j >> 3) + (j & 7) * 2) = w;
-      }
-    }
-    __syncthreads();
-#pragma unroll
-    for (int s = 0; s < 2; ++s) {
-      const int c = 2 * s + (lane >> 5);
-      u32x4 a[FM], b[FN];
-#pragma unroll
-      for (int i = 0; i < FM; ++i) a[i] = *reinterpret_cast<const u32x4*>(oA + lds_off(wm * WM + i * 32 + (lane & 31), c));
-#pragma unroll
-      for (int j = 0; j < FN; ++j) b[j] = *reinterpret_cast<const u32x4*>(oB + lds_off(wn * WN + j * 32 + (lane & 31), c));
-#pragma unroll
-      for (int i = 0; i < FM; ++i)
-#pragma unroll
-        for (int j = 0; j < FN; ++j)
-          acc[i][j] = __builtin_bit_cast(v16i, mfma16<DT>(a[i], b[j], __builtin_bit_cast(v16f, acc[i][j])));
-    }
-  }
-
-  // One rounding to the output dtype, store.
-  if constexpr (FL) {
-    // Rows R and R + 1 of a lane's column convert to one packed dword; lanes
-    // 2c and 2c + 1 trade halves of it, so the even lane holds row R of
-    // columns 2c, 2c + 1 and the odd lane row R + 1 of the same two columns:
-    // one 4-byte store per two values.  Row offsets are uniform, so the
-    // stores take a scalar base and one per-lane offset.
-    const int odd = lane & 1;
-    const uint32_t sel = odd ? 0x03020706u : 0x05040100u;  // odd: (nb.hi, own.hi), even: (own.lo, nb.lo)
-    const uint32_t loff = (uint32_t)(((4 * (lane >> 5) + odd) * N + (lane & 31) - odd) * 2);
-    const int swm = __builtin_amdgcn_readfirstlane(wm), swn = __builtin_amdgcn_readfirstlane(wn);
-    char* const ubase = reinterpret_cast<char*>(out + (m0 + swm * WM) * N + n0 + swn * WN);
-#pragma unroll
-    for (int i = 0; i < FM; ++i) {
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-#pragma unroll
-        for (int p = 0; p < 2; ++p) {
-          char* const rowp = ubase + (int64_t)(i * 32 + 8 * q + 2 * p) * N * 2;
-#pragma unroll
-          for (int j = 0; j < FN; ++j) {
-            const uint32_t pk = pack2<DT>(__int_as_float(acc[i][j][4 * q + 2 * p]),
-                                          __int_as_float(acc[i][j][4 * q + 2 * p + 1]));
-            const uint32_t nb = (uint32_t)__builtin_amdgcn_mov_dpp((int)pk, 0xB1, 0xF, 0xF, false);  // lane ^ 1
-            *reinterpret_cast<uint32_t*>(rowp + j * 64 + loff) = __builtin_amdgcn_perm(nb, pk, sel);
-          }
-        }
-      }
-    }
-  } else {
-#pragma unroll
-    for (int j = 0; j < FN; ++j) {
-      const int64_t col = cbase + j * 32;
-      bv[j] = (bias != nullptr && col < N) ? to_f32<DT>(bias[col]) : 0.0f;
-    }
-#pragma unroll
-    for (int i = 0; i < FM; ++i) {
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int64_t row = rbase + i * 32 + 8 * (r >> 2) + (r & 3);
-        if (row >= T) continue;
-        uint16_t* orow = out + row * N + cbase;
-#pragma unroll
-        for (int j = 0; j < FN; ++j)
-          if (cbase + j * 32 < N) orow[j * 32] = from_f32<DT>(__int_as_float(acc[i][j][r]) + bv[j]);
-      }
-      __builtin_amdgcn_sched_barrier(0);
-    }
-  }
+  if (n_chunks <= PF_CHUNKS && n_chunks <= wo_chunks)
+    persist_tiles<DT, 1>(CA, CB, SCA, SCB, bias, xo, idx, n_idx, out, acc_out, T, N, K, tiles_m, tiles_n, wo,
+                         wo_chunks, dA0, dA1, dB0, dB1);
+  else
+    persist_tiles<DT, 0>(CA, CB, SCA, SCB, bias, xo, idx, n_idx, out, acc_out, T, N, K, tiles_m, tiles_n, wo,
+                         wo_chunks, dA0, dA1, dB0, dB1);
 }
 
 // ---------------------------------------------------------------- decode ----
@@ -801,6 +1043,23 @@ static hipError_t launch_tile(const LinearArgs& a, hipStream_t s) {
   return hipGetLastError();
 }
 
+namespace {
+int g_gemm_cus[64];  // compute units per device, looked up once
+}
+
+static hipError_t compute_units(int& cus) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  int& c = g_gemm_cus[dev & 63];
+  if (c <= 0) {
+    e = hipDeviceGetAttribute(&c, hipDeviceAttributeMultiprocessorCount, dev);
+    if (e != hipSuccess) return e;
+  }
+  cus = c;
+  return hipSuccess;
+}
+
 template <int DT>
 static hipError_t launch_linear_t(const LinearArgs& a, hipStream_t s) {
   if (a.T <= LLI8_STREAM_MAX_T && (a.K % 16) == 0) {
@@ -816,6 +1075,20 @@ static hipError_t launch_linear_t(const LinearArgs& a, hipStream_t s) {
     return hipGetLastError();
   }
   if (a.T >= 512 && a.N >= 512 && a.K < (1 << 24)) {
+    // whole 256 x 256 tiles: one workgroup per compute unit walks its tiles
+    if (a.T % 256 == 0 && a.N % 256 == 0 && a.K % 256 == 0) {
+      int cus = 0;
+      const hipError_t e = compute_units(cus);
+      if (e != hipSuccess) return e;
+      const int tiles_m = (int)(a.T / 256), tiles_n = (int)(a.N / 256);
+      const int nb = tiles_m * tiles_n;
+      const int G = nb < cus ? nb : cus;
+      linear_persist_kernel<DT><<<dim3(G), dim3(512), 0, s>>>(
+          a.CA, a.CB, a.SCA, a.SCB, static_cast<const uint16_t*>(a.bias), static_cast<const uint16_t*>(a.xo), a.idx,
+          a.n_idx, static_cast<uint16_t*>(a.out), a.acc, (int)a.T, (int)a.N, (int)a.K, tiles_m, tiles_n,
+          static_cast<const uint16_t*>(a.wo), a.wo ? a.wo_chunks : 0);
+      return hipGetLastError();
+    }
     // direct loads: 128-byte steps in a 2-slot ring (whole cache lines per
     // row), else 64-byte steps in a 4-slot ring, else register staging
     if (a.K % 256 == 0) return launch_tile<DT, 256, 256, 128, 4, 2, 4, 2>(a, s);  // an even step count

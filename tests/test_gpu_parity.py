@@ -288,6 +288,25 @@ def test_graph_replays_match_eager(T, K, N):
         assert torch.equal(got_b, ref_b)
 
 
+@pytest.mark.parametrize("T,K,N,n_out,tau,dtype", [
+    # whole 256 x 256 tiles, more tiles than compute units: workgroups walk
+    # several tiles each, the next tile's first steps loaded during the
+    # current tile's epilogue when the outlier columns fit in registers
+    (2048, 256, 8448, 3, 6.0, "f16"),      # two K steps per tile, one chunk
+    (2048, 512, 8448, 100, 6.0, "bf16"),   # four chunks: still from registers
+    (2048, 512, 8448, 150, 6.0, "f16"),    # five chunks: staged through LDS, no cross-tile loads
+    (2048, 256, 8448, 0, 0.01, "bf16"),    # every column an outlier: no int8 product at all
+    (2048, 768, 8448, 2, 0.0, "f16"),      # threshold off: no outlier columns
+])
+def test_persistent_tiles(T, K, N, n_out, tau, dtype):
+    case = random_case(T, K, N, dtype=dtype, seed=T + K + N + n_out, n_out=n_out)
+    g, r = _check_full(case, tau)
+    if tau == 0.0:
+        assert g["n"] == 0
+    else:
+        assert g["n"] >= min(n_out, K) and (tau > 0.1 or g["n"] == K)
+
+
 @pytest.mark.parametrize("dtype", ["f16", "bf16"])
 @pytest.mark.parametrize("T,K,N,n_out,tau", [
     (600, 512, 520, 150, 6.0),    # 5 outlier chunks: 4 through the 2-slot pipeline, 1 through the ring
