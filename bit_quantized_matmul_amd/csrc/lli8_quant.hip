@@ -166,6 +166,48 @@ __device__ __forceinline__ void xo_zero_pad(uint16_t* __restrict__ xo, int total
   for (int p = total + lane; p < npad; p += WAVE) xo[xo_offset(p, row, T)] = 0;
 }
 
+// The same prologue with the bitmap words already loaded (thread t holds
+// words t and t + 256, W <= 512), and barriers that wait for LDS only: the
+// caller's row loads stay in flight through it.
+__device__ int bitmap_prefix_regs(const uint32_t (&bw)[2], int64_t W, uint32_t* words, uint32_t* prefix,
+                                  int32_t* __restrict__ idx, int32_t* __restrict__ n_idx) {
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int64_t w = threadIdx.x + 256 * i;
+    if (w < W) words[w] = bw[i];
+  }
+  __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): the words are in LDS
+  __builtin_amdgcn_s_barrier();
+  if (threadIdx.x < 64) {
+    const int lane = threadIdx.x;
+    const int64_t seg = (W + 63) / 64;
+    const int64_t w0 = lane * seg, w1 = min(W, w0 + seg);
+    int cnt = 0;
+    for (int64_t w = w0; w < w1; ++w) cnt += __popc(words[w]);
+    int run = wave_incl_scan(cnt) - cnt;
+    for (int64_t w = w0; w < w1; ++w) {
+      prefix[w] = (uint32_t)run;
+      run += __popc(words[w]);
+    }
+  }
+  __builtin_amdgcn_s_waitcnt(0xC07F);
+  __builtin_amdgcn_s_barrier();
+  const int total = (int)(prefix[W - 1] + __popc(words[W - 1]));
+  if (blockIdx.x == 0) {
+    for (int64_t w = threadIdx.x; w < W; w += blockDim.x) {
+      uint32_t m = words[w];
+      int pos = (int)prefix[w];
+      while (m) {
+        const int b = __builtin_ctz(m);
+        idx[pos++] = (int32_t)(w * 32 + b);
+        m &= m - 1u;
+      }
+    }
+    if (threadIdx.x == 0) *n_idx = total;
+  }
+  return total;
+}
+
 // One wave per row; the row stays in registers (MAXC 16-byte chunks per lane),
 // so HBM sees it once.  Requires K % 8 == 0 and K <= 512 * MAXC.
 // EXCL: activation mode (outlier columns excluded, index list, gather).
@@ -181,21 +223,31 @@ __global__ __launch_bounds__(256) void quant_rows_reg_kernel(
   extern __shared__ uint32_t lds[];
   const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
   const int64_t W = (K + 31) >> 5;
-  int total = 0;
-  if constexpr (EXCL) total = load_bitmap_prefix(bitmap, W, lds, lds + W, idx, n_idx);
-  const uint32_t* words = lds;
-  const uint32_t* prefix = lds + W;
-
+  // Activation mode: the bitmap words first, then the row, whose loads stay
+  // in flight through the bitmap prologue (R >= 1 here: rows past R re-read
+  // the last one and return before using it).
+  uint32_t bw[2] = {0u, 0u};
+  if constexpr (EXCL) {
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int64_t w = threadIdx.x + 256 * i;
+      bw[i] = bitmap[w < W ? w : W - 1];
+    }
+  }
   const int64_t row = (int64_t)blockIdx.x * 4 + wid;
-  if (row >= R) return;
   const int64_t nch = K >> 3;
-  const u32x4* rp = reinterpret_cast<const u32x4*>(src + row * K);
+  const u32x4* rp = reinterpret_cast<const u32x4*>(src + (row < R ? row : R - 1) * K);
   u32x4 v[MAXC];
 #pragma unroll
   for (int i = 0; i < MAXC; ++i) {
     const int64_t c = lane + (int64_t)i * WAVE;
     v[i] = __builtin_nontemporal_load(rp + (c < nch ? c : 0));
   }
+  int total = 0;
+  if constexpr (EXCL) total = bitmap_prefix_regs(bw, W, lds, lds + W, idx, n_idx);
+  const uint32_t* words = lds;
+  const uint32_t* prefix = lds + W;
+  if (row >= R) return;
   uint32_t ob[MAXC];  // outlier columns of each chunk (bit e); chunks past the row end count as all-outlier
 #pragma unroll
   for (int i = 0; i < MAXC; ++i) {
@@ -226,16 +278,20 @@ __global__ __launch_bounds__(256) void quant_rows_reg_kernel(
     pk[1] = pack_codes16(code_pair16<DT>(v[i][2], s), code_pair16<DT>(v[i][3], s)) & ~byte_mask4(ob[i] >> 4);
     if (c < nch) cp[c] = pk;
     if constexpr (EXCL) {
-      if (c < nch && ob[i] && xo != nullptr) {
-        const uint32_t word = words[c >> 2];
-        const int base = (int)prefix[c >> 2];
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          if ((ob[i] >> e) & 1u) {
-            const int bit = (int)((c & 3) * 8 + e);
-            const int p = base + __popc(word & ((1u << bit) - 1u));
-            xo[xo_offset(p, row, R)] = (uint16_t)half_bits(v[i], e);
-          }
+      // this chunk's outlier columns into Xo: a branch the whole wave takes
+      // or skips, then a loop over the set bits (an unrolled test per column
+      // would keep a mask per column live and spill them)
+      uint32_t f = (c < nch && xo != nullptr) ? ob[i] : 0u;
+      if (__ballot(f != 0u) != 0) {
+        const int64_t cw = (c < nch ? c : 0) >> 2;
+        const uint32_t word = words[cw];
+        const int base = (int)prefix[cw];
+        while (f) {
+          const int e = __builtin_ctz(f);
+          f &= f - 1u;
+          const int bit = (int)((c & 3) * 8 + e);
+          const int p = base + __popc(word & ((1u << bit) - 1u));
+          xo[xo_offset(p, row, R)] = (uint16_t)half_bits(v[i], e);
         }
       }
     }
@@ -305,7 +361,9 @@ static hipError_t launch_quant_rows_t(const uint16_t* src, int64_t R, int64_t K,
   if (blocks == 0) return hipSuccess;
   const size_t lds = EXCL ? (size_t)2 * ((K + 31) / 32) * sizeof(uint32_t) : 0;
   dim3 grid((unsigned)blocks), block(256);
-  if ((K & 7) == 0 && K <= 512 * 2)
+  if (R == 0)  // activation mode, no rows: index list and count only
+    quant_rows_any_kernel<DT, EXCL><<<grid, block, lds, s>>>(src, R, K, codes, scales, bitmap, idx, n_idx, xo);
+  else if ((K & 7) == 0 && K <= 512 * 2)
     quant_rows_reg_kernel<DT, EXCL, 2><<<grid, block, lds, s>>>(src, R, K, codes, scales, bitmap, idx, n_idx, xo);
   else if ((K & 7) == 0 && K <= 512 * 8)
     quant_rows_reg_kernel<DT, EXCL, 8><<<grid, block, lds, s>>>(src, R, K, codes, scales, bitmap, idx, n_idx, xo);
