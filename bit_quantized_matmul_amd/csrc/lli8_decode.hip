@@ -319,7 +319,7 @@ __global__ __launch_bounds__(FD_THREADS, 1) void decode_fused_kernel(
           const int rank = (int)pre + __popc(s_bm[word] & ((1u << (col & 31)) - 1u));
           if (rank < FD_OUT_LDS) {
             const int8_t cb = (int8_t)((b[m][e >> 2] >> (8 * (e & 3))) & 0xFFu);
-            s_ow[rank][nr] = to_f32<DT>(from_f32<DT>(((float)cb * scb_n) / 127.0f));
+            s_ow[rank][nr] = to_f32<DT>(from_f32<DT>(div127((float)cb * scb_n)));
           }
         }
       }
@@ -379,7 +379,7 @@ __global__ __launch_bounds__(FD_THREADS, 1) void decode_fused_kernel(
         if (col < N) {
           for (int p = n_lds; p < n_out; ++p) {  // beyond the LDS stage: straight from memory
             const int cc = s_idx[p];
-            const float wv = to_f32<DT>(from_f32<DT>(((float)CB[col * K + cc] * scb_n) / 127.0f));
+            const float wv = to_f32<DT>(from_f32<DT>(div127((float)CB[col * K + cc] * scb_n)));
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
               const int t = 4 * q + r;

@@ -39,6 +39,22 @@ __device__ __forceinline__ uint16_t from_f32(float v) {
   }
 }
 
+// fl32(p / 127), correctly rounded.  For 2^-100 <= |p| < 2^101 and for zero
+// one multiply by fl32(1/127) and one FMA correction give the same bits as
+// the IEEE division (checked on the device against the division for every
+// float in that range, both signs); other values (tiny, huge, inf, NaN) take
+// the division itself.
+__device__ __forceinline__ float div127(float p) {
+  constexpr float r = 1.0f / 127.0f;
+  const float a = __builtin_fabsf(p);
+  if (a < 0x1p101f && (a >= 0x1p-100f || a == 0.0f)) {
+    const float q0 = p * r;
+    const float e = __builtin_fmaf(-q0, 127.0f, p);  // exact remainder
+    return __builtin_fmaf(e, r, q0);
+  }
+  return p / 127.0f;
+}
+
 // Element e (0..7) of a 16-byte chunk of eight 16-bit values.
 __device__ __forceinline__ uint32_t half_bits(const u32x4& c, int e) {
   uint32_t w = c[e >> 1];

@@ -50,7 +50,7 @@ __device__ __forceinline__ int lds_off(int r, int c) { return tile_off<64>(r, c)
 template <int DT>
 __device__ __forceinline__ uint16_t recover_w(int8_t cb, float scb) {
   const float p = (float)cb * scb;
-  return from_f32<DT>(p / 127.0f);
+  return from_f32<DT>(div127(p));
 }
 
 // Two fp32 values rounded (to nearest even) to the 16-bit dtype and packed,

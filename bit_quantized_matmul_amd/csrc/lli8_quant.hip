@@ -407,11 +407,19 @@ __global__ __launch_bounds__(256) void recover_outliers_kernel(
     const int32_t* __restrict__ idx, const int32_t* __restrict__ n_idx_p, uint16_t* __restrict__ wo, int chunks) {
   const int total = *n_idx_p;
   const int used = min((total + 31) >> 5, chunks);
-  const int64_t per_row = (int64_t)used * 4;  // pieces per row
-  const int64_t pieces = per_row * N;
+  // Piece q: part q % 4 of row 16 b + (q / 4) % 16 of chunk (q / 64) % used,
+  // b = q / (64 used).  A wave writes 16 consecutive 64-byte rows of one
+  // chunk (1 KiB, contiguous) and the next wave the same rows' next chunk,
+  // whose CB bytes lie in the lines just read.
+  const int64_t nblk = (N + 15) >> 4;
+  const int64_t pieces = nblk * used * 64;
   for (int64_t q = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; q < pieces; q += (int64_t)gridDim.x * blockDim.x) {
-    const int64_t n = q / per_row;
-    const int cp = (int)(q - n * per_row);  // chunk * 4 + part
+    const int64_t g = q >> 6;  // (row block, chunk)
+    const int64_t b = g / used;
+    const int ch = (int)(g - b * used);
+    const int64_t n = b * 16 + ((q >> 2) & 15);
+    if (n >= N) continue;
+    const int cp = ch * 4 + (int)(q & 3);  // chunk * 4 + part
     const int p0 = cp * 8;
     const float scb = SCB[n];
     const int8_t* cbrow = CB + n * K;
@@ -428,14 +436,14 @@ __global__ __launch_bounds__(256) void recover_outliers_kernel(
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
         const int8_t cb = (int8_t)(((e < 4 ? lo : hi) >> (8 * (e & 3))) & 0xFFu);
-        const uint32_t w = from_f32<DT>(((float)cb * scb) / 127.0f);
+        const uint32_t w = from_f32<DT>(div127((float)cb * scb));
         v[e >> 1] |= w << (16 * (e & 1));
       }
     } else {
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
         if (p0 + e < total) {
-          const uint32_t w = from_f32<DT>(((float)cbrow[idx[p0 + e]] * scb) / 127.0f);
+          const uint32_t w = from_f32<DT>(div127((float)cbrow[idx[p0 + e]] * scb));
           v[e >> 1] |= w << (16 * (e & 1));
         }
       }
@@ -451,7 +459,7 @@ hipError_t launch_recover_outliers(int dt, const int8_t* CB, const float* SCB, i
   // covers up to four (128 outlier columns: one piece per thread); the loop
   // walks any more.  A grid sized for every chunk the scratch can hold would
   // be mostly workgroups with nothing to do.
-  const int64_t most = (int64_t)(chunks < 4 ? chunks : 4) * 4 * N;
+  const int64_t most = (int64_t)(chunks < 4 ? chunks : 4) * 64 * ((N + 15) / 16);
   const int64_t want = (most + 255) / 256;
   const int64_t blocks = want < 4096 ? want : 4096;
   uint16_t* w = static_cast<uint16_t*>(wo);

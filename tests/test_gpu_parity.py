@@ -317,3 +317,35 @@ def test_many_outlier_chunks_large_tiles(T, K, N, n_out, tau, dtype):
     case = random_case(T, K, N, dtype=dtype, seed=T + K + n_out, n_out=n_out)
     g, r = _check_full(case, tau)
     assert g["n"] >= min(n_out, K) and (tau > 0.1 or g["n"] == K)
+
+
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+def test_recovered_weights_bit_exact(dtype):
+    """The recovered outlier weights the tile path writes to scratch (chunk-major
+    [chunk][N][32], zero past n) equal the oracle's dtype(fl32(fl32(CB * SCB) /
+    127)) bit for bit.  For bf16 some weight rows are scaled far down or up, so
+    that products below 2^-100 and above 2^101 take the full division and the
+    rest the multiply-and-correct form."""
+    B = _lib()
+    import torch
+    T, K, N = 256, 512, 300
+    case = random_case(T, K, N, dtype=dtype, seed=77, n_out=40)
+    Wb = case.W
+    if dtype == "bf16":
+        vals = O.decode_bits(Wb, dtype).astype(np.float64)
+        vals[0::7] *= 1e-34
+        vals[3::11] *= 1e34
+        Wb = O.round_to_dtype_bits(vals, dtype)
+    CB, SCB = B.lli8_quant_weight_rowwise(to_dev(Wb, dtype))
+    _, ws = B.lli8_int8_linear(to_dev(case.X, dtype), CB, SCB, None, 6.0)
+    torch.cuda.synchronize()
+    n = int(ws.n_idx.item())
+    assert n >= 40
+    idx = ws.idx[:n].cpu().numpy()
+    chunks = (n + 31) // 32
+    xb = T * ((K + 31) // 32 * 32) * 2
+    wo = ws.scratch[xb:xb + chunks * N * 64].cpu().numpy().view(np.uint16).reshape(chunks, N, 32)
+    got = O.decode_bits(wo.transpose(1, 0, 2).reshape(N, chunks * 32), dtype).astype(np.float64)
+    ref = O.recover_weight(CB.cpu().numpy()[:, idx], SCB.cpu().numpy(), dtype)
+    np.testing.assert_array_equal(got[:, :n], ref)
+    assert not got[:, n:].any()
