@@ -833,8 +833,13 @@ __device__ __forceinline__ void persist_tiles(
     __builtin_amdgcn_s_barrier();
     __builtin_amdgcn_sched_barrier(0);
   };
-  int8_t* const ring_a[4] = {dA0, dA1, dA1, dA1};
-  int8_t* const ring_b[4] = {dB0, dB1, dB1, dB1};
+  // Staged outlier chunks (PF = 0) are 64-byte rows, so one chunk's A and B
+  // fit in one of the four 32 KiB LDS objects: a 4-slot ring with three
+  // chunks in flight, each slot an object of its own (so the compiler can
+  // tell the slot being read from those being filled).
+  int8_t* const ring_a[4] = {dA0, dA1, dB0, dB1};
+  int8_t* const ring_b[4] = {dA0 + BM * 64, dA1 + BM * 64, dB0 + BM * 64, dB1 + BM * 64};
+  static_assert(BM * 64 + BN * 64 <= BM * BK && BN == BM, "a chunk's two operands fit one ring object");
 
   bool first = true;
   for (int v = blockIdx.x; v < nb; v += gridDim.x) {
@@ -890,7 +895,7 @@ __device__ __forceinline__ void persist_tiles(
       __builtin_amdgcn_sched_barrier(0);
     }
     if constexpr (!PF) __syncthreads();  // the epilogue may stage through LDS
-    tile_epilogue<DT, BM, BN, WGM, WGN, 2, 1, PF>(
+    tile_epilogue<DT, BM, BN, WGM, WGN, 4, 1, PF>(
         acc, m0, n0, T, N, K, SCA, SCB, bias, xo, idx, n_idx, CB, wo, wo_chunks, out, acc_out, ring_a, ring_b,
         [&] {
           // the next tile's second step, once every wave is past the last
