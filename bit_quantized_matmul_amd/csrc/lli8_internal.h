@@ -14,6 +14,11 @@ hipError_t launch_quant_weight(int dt, const void* W, int64_t N, int64_t K, int8
 hipError_t launch_scan_outliers(int dt, const void* X, int64_t T, int64_t K, float tau,
                                 uint32_t* bitmap, hipStream_t s);
 
+// True when launch_scan_outliers writes every bitmap word itself (few rows:
+// one workgroup per column strip covers all of them), so the bitmap needs no
+// clearing beforehand; otherwise it ORs into a zeroed bitmap.
+bool scan_writes_all_words(int64_t T, int64_t K);
+
 hipError_t launch_quant_act(int dt, const void* X, int64_t T, int64_t K, const uint32_t* bitmap,
                             int8_t* CA, float* SCA, int32_t* idx, int32_t* n_idx, void* xo,
                             hipStream_t s);
