@@ -349,3 +349,35 @@ def test_recovered_weights_bit_exact(dtype):
     ref = O.recover_weight(CB.cpu().numpy()[:, idx], SCB.cpu().numpy(), dtype)
     np.testing.assert_array_equal(got[:, :n], ref)
     assert not got[:, n:].any()
+
+
+def _sweep_case(seed):
+    """A seeded random shape across the launch routes: whole 256 x 256 tiles
+    (persistent kernel), few rows (strip scan, weight streaming, small tiles),
+    ragged large shapes and small ones; either dtype, a few outlier counts and
+    thresholds."""
+    rng = np.random.default_rng(1000 + seed)
+    kind = seed % 4
+    if kind == 0:
+        T, N, K = 256 * int(rng.integers(2, 9)), 256 * int(rng.integers(2, 40)), 256 * int(rng.integers(1, 9))
+    elif kind == 1:
+        T, N, K = int(rng.integers(1, 300)), int(rng.integers(1, 3000)), 8 * int(rng.integers(1, 600))
+    elif kind == 2:
+        T, N, K = int(rng.integers(500, 1500)), int(rng.integers(500, 3000)), int(rng.integers(1, 1200))
+    else:
+        T, N, K = int(rng.integers(1, 200)), int(rng.integers(1, 500)), int(rng.integers(1, 700))
+    if T * N * K > 3e8:  # keep the oracle quick
+        if kind == 0:
+            N = max(256, int(3e8 // (T * K)) // 256 * 256)
+        else:
+            K = max(1, int(3e8 // (T * N)))
+    dtype = "f16" if rng.integers(0, 2) == 0 else "bf16"
+    n_out = int(rng.choice([0, 1, 3, 17, 40, 150]))
+    tau = float(rng.choice([6.0, 6.0, 6.0, 2.5, 0.0]))
+    return random_case(T, K, N, dtype=dtype, seed=int(rng.integers(0, 1 << 30)), n_out=min(n_out, K)), tau
+
+
+@pytest.mark.parametrize("seed", range(48))
+def test_random_sweep(seed):
+    case, tau = _sweep_case(seed)
+    _check_full(case, tau)
