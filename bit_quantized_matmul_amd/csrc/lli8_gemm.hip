@@ -927,22 +927,29 @@ __global__ __launch_bounds__(512) void linear_persist_kernel(
 }
 
 // ---------------------------------------------------------------- decode ----
-// T <= 16 MB, K % 16 == 0.  Workgroup = 16 output features; wave w takes the
-// 256-byte K slices w, w + 4, ...; lane (n, g) = (lane % 16, lane / 16) loads
-// 64 contiguous bytes of weight row n once and, for each block of 16 tokens,
-// the matching activation bytes, which feed four 16x16x64 MFMAs per block (A
-// and B use the same K permutation, so the dot products are exact).  The
-// weight rows are streamed once whatever T is; N / 16 workgroups fill the
-// chip.  Partial int32 tiles are summed through LDS in a fixed order
-// (deterministic).
-template <int DT, int MB>
-__global__ __launch_bounds__(256) void linear_decode_kernel(
+// T <= 16 MB, K % 16 == 0.  Workgroup = 16 output features in NW waves;
+// wave w takes the 256-byte K slices w, w + NW, ...  Lane (n, g) = (lane %
+// 16, lane / 16) loads bytes 16 g + 64 u .. + 15 (u = 0 .. 3) of the slice of
+// weight row n once and, for each block of 16 tokens, the matching
+// activation bytes, which feed four 16x16x64 MFMAs per block (A and B use
+// the same K permutation, so the dot products are exact).  So each load
+// instruction reads one whole 64-byte sector of each of 16 rows; lanes that
+// read 64 contiguous bytes each touched four sectors per row and
+// instruction and streamed at little more than half the rate (with whole
+// sectors, 4, 8 and 16 waves measure alike).  The weight rows are streamed
+// once whatever T is; N / 16 workgroups fill the chip.  The waves' int32
+// tiles are summed with LDS integer atomics (exact in any order), and wave mb
+// runs the epilogue of token block mb.
+template <int DT, int MB, int NW>
+__global__ __launch_bounds__(NW * 64) void linear_decode_kernel(
     const int8_t* __restrict__ CA, const int8_t* __restrict__ CB, const float* __restrict__ SCA,
     const float* __restrict__ SCB, const uint16_t* __restrict__ bias, const uint16_t* __restrict__ xo,
     const int32_t* __restrict__ idx, const int32_t* __restrict__ n_idx_p, uint16_t* __restrict__ out,
     int32_t* __restrict__ acc_out, int T, int N, int K) {
-  __shared__ v4i red[3][MB][64];
+  static_assert(NW >= MB, "one wave per token block in the epilogue");
+  __shared__ int32_t red[MB][4][64];
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  for (int i = tid; i < MB * 256; i += NW * 64) (&red[0][0][0])[i] = 0;
   const int64_t n0 = (int64_t)blockIdx.x * 16;
   const int nr = lane & 15, g = lane >> 4;
   const int64_t n = n0 + nr;
@@ -951,12 +958,12 @@ __global__ __launch_bounds__(256) void linear_decode_kernel(
 #pragma unroll
   for (int mb = 0; mb < MB; ++mb) acc[mb] = (v4i){0, 0, 0, 0};
   const int8_t* brow = CB + n * (int64_t)K;
-  for (int s = w; s < nss; s += 4) {
-    const int64_t kb = (int64_t)s * 256 + g * 64;
+  for (int s = w; s < nss; s += NW) {
+    const int64_t kb = (int64_t)s * 256 + g * 16;
     u32x4 b[4];
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
-      const int64_t k = kb + 16 * u;
+      const int64_t k = kb + 64 * u;
       b[u] = (n < N && k < K) ? __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(brow + k))
                               : (u32x4){0u, 0u, 0u, 0u};
     }
@@ -967,7 +974,7 @@ __global__ __launch_bounds__(256) void linear_decode_kernel(
       u32x4 a[4];
 #pragma unroll
       for (int u = 0; u < 4; ++u) {
-        const int64_t k = kb + 16 * u;
+        const int64_t k = kb + 64 * u;
         a[u] = (t < T && k < K) ? *reinterpret_cast<const u32x4*>(arow + k) : (u32x4){0u, 0u, 0u, 0u};
       }
 #pragma unroll
@@ -976,18 +983,17 @@ __global__ __launch_bounds__(256) void linear_decode_kernel(
                                                         acc[mb], 0, 0, 0);
     }
   }
-  if (w > 0) {
+  __syncthreads();  // the zeroed sums are in place
 #pragma unroll
-    for (int mb = 0; mb < MB; ++mb) red[w - 1][mb][lane] = acc[mb];
-  }
+  for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) atomicAdd(&red[mb][r][lane], acc[mb][r]);
   __syncthreads();
-  if (w != 0) return;
+  if (w >= MB) return;
+  const int mb = w;  // this wave's block of 16 tokens
+  v4i sum;
 #pragma unroll
-  for (int mb = 0; mb < MB; ++mb) {
-    acc[mb] += red[0][mb][lane];
-    acc[mb] += red[1][mb][lane];
-    acc[mb] += red[2][mb][lane];
-  }
+  for (int r = 0; r < 4; ++r) sum[r] = red[mb][r][lane];
 
   // 16x16 accumulator layout: lane holds column lane % 16, rows 4 * (lane / 16) + r
   // of its block of 16 tokens.
@@ -996,31 +1002,23 @@ __global__ __launch_bounds__(256) void linear_decode_kernel(
   if (col >= N) return;
   const float scb = SCB[col];
   const float bv = (bias != nullptr) ? to_f32<DT>(bias[col]) : 0.0f;
-  float o[MB][4];
-#pragma unroll
-  for (int mb = 0; mb < MB; ++mb)
-#pragma unroll
-    for (int r = 0; r < 4; ++r) o[mb][r] = 0.0f;
+  float o[4] = {0.0f, 0.0f, 0.0f, 0.0f};
   for (int p = 0; p < n_idx; ++p) {
     const float wv = to_f32<DT>(recover_w<DT>(CB[col * K + idx[p]], scb));
 #pragma unroll
-    for (int mb = 0; mb < MB; ++mb)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int t = 16 * mb + 4 * (lane >> 4) + r;
-        if (t < T) o[mb][r] += to_f32<DT>(xo[((int64_t)(p >> 5) * T + t) * 32 + (p & 31)]) * wv;
-      }
-  }
-#pragma unroll
-  for (int mb = 0; mb < MB; ++mb)
-#pragma unroll
     for (int r = 0; r < 4; ++r) {
       const int t = 16 * mb + 4 * (lane >> 4) + r;
-      if (t >= T) continue;
-      if (acc_out != nullptr) acc_out[(int64_t)t * N + col] = acc[mb][r];
-      const float d = (float)acc[mb][r] * (SCA[t] * (scb * (1.0f / 16129.0f)));
-      out[(int64_t)t * N + col] = from_f32<DT>(d + o[mb][r] + bv);
+      if (t < T) o[r] += to_f32<DT>(xo[((int64_t)(p >> 5) * T + t) * 32 + (p & 31)]) * wv;
     }
+  }
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    const int t = 16 * mb + 4 * (lane >> 4) + r;
+    if (t >= T) continue;
+    if (acc_out != nullptr) acc_out[(int64_t)t * N + col] = sum[r];
+    const float d = (float)sum[r] * (SCA[t] * (scb * (1.0f / 16129.0f)));
+    out[(int64_t)t * N + col] = from_f32<DT>(d + o[r] + bv);
+  }
 }
 
 template <int DT, int BM, int BN, int BK, int WGM, int WGN, int GM = 8, int DL = 0>
@@ -1070,11 +1068,12 @@ static hipError_t launch_linear_t(const LinearArgs& a, hipStream_t s) {
   if (a.T <= LLI8_STREAM_MAX_T && (a.K % 16) == 0) {
     // weight-streaming kernel: every weight row read once, N / 16 workgroups
     const int nb = (int)((a.N + 15) / 16);
-    decltype(&linear_decode_kernel<DT, 1>) k = a.T <= 16 ? linear_decode_kernel<DT, 1>
-                                              : a.T <= 32 ? linear_decode_kernel<DT, 2>
-                                              : a.T <= 64 ? linear_decode_kernel<DT, 4>
-                                                          : linear_decode_kernel<DT, 8>;
-    k<<<dim3(nb), dim3(256), 0, s>>>(
+    constexpr int NW = 8;
+    decltype(&linear_decode_kernel<DT, 1, NW>) k = a.T <= 16 ? linear_decode_kernel<DT, 1, NW>
+                                                  : a.T <= 32 ? linear_decode_kernel<DT, 2, NW>
+                                                  : a.T <= 64 ? linear_decode_kernel<DT, 4, NW>
+                                                              : linear_decode_kernel<DT, 8, NW>;
+    k<<<dim3(nb), dim3(NW * 64), 0, s>>>(
         a.CA, a.CB, a.SCA, a.SCB, static_cast<const uint16_t*>(a.bias), static_cast<const uint16_t*>(a.xo),
         a.idx, a.n_idx, static_cast<uint16_t*>(a.out), a.acc, (int)a.T, (int)a.N, (int)a.K);
     return hipGetLastError();
