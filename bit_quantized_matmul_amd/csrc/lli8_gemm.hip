@@ -928,15 +928,15 @@ __global__ __launch_bounds__(512) void linear_persist_kernel(
 
 // ---------------------------------------------------------------- decode ----
 // T <= 16 MB, K % 16 == 0.  Workgroup = 16 output features in NW waves;
-// wave w takes the 256-byte K slices w, w + NW, ...  Lane (n, g) = (lane %
-// 16, lane / 16) loads bytes 16 g + 64 u .. + 15 (u = 0 .. 3) of the slice of
-// weight row n once and, for each block of 16 tokens, the matching
-// activation bytes, which feed four 16x16x64 MFMAs per block (A and B use
-// the same K permutation, so the dot products are exact).  So each load
-// instruction reads one whole 64-byte sector of each of 16 rows; lanes that
-// read 64 contiguous bytes each touched four sectors per row and
-// instruction and streamed at little more than half the rate (with whole
-// sectors, 4, 8 and 16 waves measure alike).  The weight rows are streamed
+// wave w takes the 256-byte K slices w, w + NW, ... and issues all of a
+// slice's loads before its first MFMA.  Lane (n, g) = (lane % 16, lane / 16)
+// loads bytes 16 g + 64 u .. + 15 (u = 0 .. 3) of the slice of weight row n
+// once and, for each block of 16 tokens, the matching activation bytes,
+// which feed four 16x16x64 MFMAs per block (A and B use the same K
+// permutation, so the dot products are exact).  So each load instruction
+// reads one whole 64-byte sector of each of 16 rows; lanes that read 64
+// contiguous bytes each touched four sectors per row and instruction and
+// streamed at little more than half the rate.  The weight rows are streamed
 // once whatever T is; N / 16 workgroups fill the chip.  The waves' int32
 // tiles are summed with LDS integer atomics (exact in any order), and wave mb
 // runs the epilogue of token block mb.
@@ -952,36 +952,44 @@ __global__ __launch_bounds__(NW * 64) void linear_decode_kernel(
   for (int i = tid; i < MB * 256; i += NW * 64) (&red[0][0][0])[i] = 0;
   const int64_t n0 = (int64_t)blockIdx.x * 16;
   const int nr = lane & 15, g = lane >> 4;
-  const int64_t n = n0 + nr;
   const int nss = (K + 255) >> 8;
   v4i acc[MB];
 #pragma unroll
   for (int mb = 0; mb < MB; ++mb) acc[mb] = (v4i){0, 0, 0, 0};
-  const int8_t* brow = CB + n * (int64_t)K;
+  // Buffer loads: a read outside its resource returns zeros, so weight rows
+  // past N, token rows past T and columns past K (offset pushed out of range)
+  // need no branch.  A per-lane condition around each load became a branch,
+  // and the compiler waited for every load in flight before each one: one
+  // memory round trip per block of 16 tokens.
+  constexpr int OOB = 0x7FFFFFF0;  // beyond any resource here (sizes < 2^31 bytes)
+  const __amdgpu_buffer_rsrc_t rb = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)(CB + n0 * (int64_t)K), 0, (N - (int)n0 < 16 ? N - (int)n0 : 16) * K, 0x00020000);
+  const __amdgpu_buffer_rsrc_t ra = __builtin_amdgcn_make_buffer_rsrc((void*)CA, 0, T * K, 0x00020000);
   for (int s = w; s < nss; s += NW) {
-    const int64_t kb = (int64_t)s * 256 + g * 16;
+    const int kb = s * 256 + g * 16;
     u32x4 b[4];
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
-      const int64_t k = kb + 64 * u;
-      b[u] = (n < N && k < K) ? __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(brow + k))
-                              : (u32x4){0u, 0u, 0u, 0u};
+      const int k = kb + 64 * u;
+      b[u] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rb, k < K ? nr * K + k : OOB, 0, 2));
     }
+    u32x4 a[MB][4];
 #pragma unroll
-    for (int mb = 0; mb < MB; ++mb) {
-      const int t = 16 * mb + nr;
-      const int8_t* arow = CA + (int64_t)t * K;
-      u32x4 a[4];
+    for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
       for (int u = 0; u < 4; ++u) {
-        const int64_t k = kb + 64 * u;
-        a[u] = (t < T && k < K) ? *reinterpret_cast<const u32x4*>(arow + k) : (u32x4){0u, 0u, 0u, 0u};
+        const int k = kb + 64 * u;
+        a[mb][u] = __builtin_bit_cast(
+            u32x4, __builtin_amdgcn_raw_buffer_load_b128(ra, k < K ? (16 * mb + nr) * K + k : OOB, 0, 0));
       }
+    // every load of the slice in flight before the first MFMA waits for one
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
       for (int u = 0; u < 4; ++u)
-        acc[mb] = __builtin_amdgcn_mfma_i32_16x16x64_i8(__builtin_bit_cast(v4i, a[u]), __builtin_bit_cast(v4i, b[u]),
-                                                        acc[mb], 0, 0, 0);
-    }
+        acc[mb] = __builtin_amdgcn_mfma_i32_16x16x64_i8(__builtin_bit_cast(v4i, a[mb][u]),
+                                                        __builtin_bit_cast(v4i, b[u]), acc[mb], 0, 0, 0);
   }
   __syncthreads();  // the zeroed sums are in place
 #pragma unroll
@@ -1002,13 +1010,34 @@ __global__ __launch_bounds__(NW * 64) void linear_decode_kernel(
   if (col >= N) return;
   const float scb = SCB[col];
   const float bv = (bias != nullptr) ? to_f32<DT>(bias[col]) : 0.0f;
+  // Outlier columns eight at a time: a group's loads all go out before any
+  // of its arithmetic (indices clamped into range and the surplus products
+  // zeroed, rather than loads behind conditions or next to the division's
+  // branch, which the compiler waits on), then the products are added in
+  // column order.
   float o[4] = {0.0f, 0.0f, 0.0f, 0.0f};
-  for (int p = 0; p < n_idx; ++p) {
-    const float wv = to_f32<DT>(recover_w<DT>(CB[col * K + idx[p]], scb));
+  for (int p0 = 0; p0 < n_idx; p0 += 8) {
+    int8_t cb[8];
+    uint16_t xb[8][4];
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int t = 16 * mb + 4 * (lane >> 4) + r;
-      if (t < T) o[r] += to_f32<DT>(xo[((int64_t)(p >> 5) * T + t) * 32 + (p & 31)]) * wv;
+    for (int j = 0; j < 8; ++j) {
+      const int p = p0 + j < n_idx ? p0 + j : n_idx - 1;
+      cb[j] = CB[col * K + idx[p]];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int t = 16 * mb + 4 * (lane >> 4) + r;
+        xb[j][r] = xo[((int64_t)(p >> 5) * T + (t < T ? t : T - 1)) * 32 + (p & 31)];
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const bool okp = p0 + j < n_idx;
+      const float wv = to_f32<DT>(recover_w<DT>(cb[j], scb));
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int t = 16 * mb + 4 * (lane >> 4) + r;
+        if (okp && t < T) o[r] += to_f32<DT>(xb[j][r]) * wv;
+      }
     }
   }
 #pragma unroll
@@ -1068,12 +1097,13 @@ static hipError_t launch_linear_t(const LinearArgs& a, hipStream_t s) {
   if (a.T <= LLI8_STREAM_MAX_T && (a.K % 16) == 0) {
     // weight-streaming kernel: every weight row read once, N / 16 workgroups
     const int nb = (int)((a.N + 15) / 16);
-    constexpr int NW = 8;
-    decltype(&linear_decode_kernel<DT, 1, NW>) k = a.T <= 16 ? linear_decode_kernel<DT, 1, NW>
-                                                  : a.T <= 32 ? linear_decode_kernel<DT, 2, NW>
-                                                  : a.T <= 64 ? linear_decode_kernel<DT, 4, NW>
-                                                              : linear_decode_kernel<DT, 8, NW>;
-    k<<<dim3(nb), dim3(NW * 64), 0, s>>>(
+    // 16 waves (one 256-byte slice each at K = 4096) while a wave's
+    // activation fragments fit in 128 registers, else 8
+    decltype(&linear_decode_kernel<DT, 1, 16>) k = a.T <= 16 ? linear_decode_kernel<DT, 1, 16>
+                                                  : a.T <= 32 ? linear_decode_kernel<DT, 2, 16>
+                                                  : a.T <= 64 ? linear_decode_kernel<DT, 4, 16>
+                                                              : linear_decode_kernel<DT, 8, 8>;
+    k<<<dim3(nb), dim3(a.T <= 64 ? 16 * 64 : 8 * 64), 0, s>>>(
         a.CA, a.CB, a.SCA, a.SCB, static_cast<const uint16_t*>(a.bias), static_cast<const uint16_t*>(a.xo),
         a.idx, a.n_idx, static_cast<uint16_t*>(a.out), a.acc, (int)a.T, (int)a.N, (int)a.K);
     return hipGetLastError();

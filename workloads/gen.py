@@ -134,7 +134,8 @@ def make_case(name: str, T: int, K: int, N: int, dtype: str = F16, *,
                 weights_each_call)
 
 
-# The five workloads, plus the clamped-base variant of the stress case.
+# The workloads: the pages' five, a 64-token decode batch, and the
+# clamped-base variant of the stress case.
 CONFIGS = {
     # 64->64 layer with bias, two planted outlier columns.
     "tiny": dict(T=8, K=64, N=64, dtype=F16, fixed_cols=[3, 17], out_lo=8.0,
@@ -142,6 +143,10 @@ CONFIGS = {
     # 16-token decode step of a 4096->4096 projection; weights pre-quantized.
     "decode": dict(T=16, K=4096, N=4096, dtype=F16, n_out=6, w_sigma=0.02,
                    bias="zero"),
+    # The same projection for a batch of 64 tokens: past the fused one-launch
+    # path, on the weight-streaming GEMM (a small-batch serving step).
+    "decode_b64": dict(T=64, K=4096, N=4096, dtype=F16, n_out=6, w_sigma=0.02,
+                       bias="zero"),
     # 4096-token prefill through a 7B-class MLP up-projection.
     "prefill_mlp_up": dict(T=4096, K=4096, N=11008, dtype=F16, n_out=4,
                            w_sigma=0.02),
@@ -159,8 +164,8 @@ CONFIGS = {
                                 weights_each_call=True),
 }
 
-CONFIG_ORDER = ["tiny", "decode", "prefill_mlp_up", "ffn_175b", "stress_bf16",
-                "stress_bf16_clamped"]
+CONFIG_ORDER = ["tiny", "decode", "decode_b64", "prefill_mlp_up", "ffn_175b",
+                "stress_bf16", "stress_bf16_clamped"]
 
 
 def config_case(name: str, seed: int = 0) -> Case:
