@@ -939,7 +939,8 @@ __global__ __launch_bounds__(512) void linear_persist_kernel(
 // streamed at little more than half the rate.  The weight rows are streamed
 // once whatever T is; N / 16 workgroups fill the chip.  The waves' int32
 // tiles are summed with LDS integer atomics (exact in any order), and wave mb
-// runs the epilogue of token block mb.
+// runs the epilogue of token block mb, whose operands that do not depend on
+// the product it requested behind its first slice's loads.
 template <int DT, int MB, int NW>
 __global__ __launch_bounds__(NW * 64) void linear_decode_kernel(
     const int8_t* __restrict__ CA, const int8_t* __restrict__ CB, const float* __restrict__ SCA,
@@ -965,6 +966,45 @@ __global__ __launch_bounds__(NW * 64) void linear_decode_kernel(
   const __amdgpu_buffer_rsrc_t rb = __builtin_amdgcn_make_buffer_rsrc(
       (void*)(CB + n0 * (int64_t)K), 0, (N - (int)n0 < 16 ? N - (int)n0 : 16) * K, 0x00020000);
   const __amdgpu_buffer_rsrc_t ra = __builtin_amdgcn_make_buffer_rsrc((void*)CA, 0, T * K, 0x00020000);
+
+  // The epilogue's operands that do not depend on the product are requested
+  // right behind the first slice's loads, so they arrive during the stream:
+  // the column's scale and bias, the tokens' scales, and the weight bytes and
+  // activations of the first eight outlier columns (indices clamped into
+  // range; entries past n_idx are read but never used, and with no gathered
+  // columns the activation reads are out of their resource and return 0).
+  // Wave w < MB requests those of token block w.
+  const int mbe = w < MB ? w : MB - 1;
+  const int64_t col = n0 + nr;
+  const int64_t colc = col < N ? col : (int64_t)N - 1;
+  const uint16_t* bsrc = (bias != nullptr) ? bias : reinterpret_cast<const uint16_t*>(SCB);
+  const uint32_t bmask = (bias != nullptr) ? 0xFFFFu : 0u;
+  int tt[4];
+#pragma unroll
+  for (int r = 0; r < 4; ++r) tt[r] = 16 * mbe + 4 * g + r;
+  float scb, sca[4];
+  uint32_t braw;
+  int8_t cb0[8];
+  u32x4 xq0[4];
+  auto prefetch_epilogue = [&]() {
+    scb = SCB[colc];
+    braw = bsrc[colc];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) sca[r] = SCA[tt[r] < T ? tt[r] : T - 1];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {  // idx holds K >= 16 entries
+      const int c = idx[j];
+      cb0[j] = CB[colc * K + (c < 0 ? 0 : (c >= K ? K - 1 : c))];
+    }
+    // chunk 0 of the gathered activations: row t, columns 0 .. 7 in 16 bytes
+    const __amdgpu_buffer_rsrc_t rx = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)(xo != nullptr ? xo : reinterpret_cast<const uint16_t*>(CB)), 0, xo != nullptr ? T * 64 : 0,
+        0x00020000);
+#pragma unroll
+    for (int r = 0; r < 4; ++r)
+      xq0[r] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rx, (tt[r] < T ? tt[r] : T - 1) * 64, 0, 0));
+  };
+
   for (int s = w; s < nss; s += NW) {
     const int kb = s * 256 + g * 16;
     u32x4 b[4];
@@ -982,6 +1022,7 @@ __global__ __launch_bounds__(NW * 64) void linear_decode_kernel(
         a[mb][u] = __builtin_bit_cast(
             u32x4, __builtin_amdgcn_raw_buffer_load_b128(ra, k < K ? (16 * mb + nr) * K + k : OOB, 0, 0));
       }
+    if (s == w && w < MB) prefetch_epilogue();
     // every load of the slice in flight before the first MFMA waits for one
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
@@ -991,6 +1032,7 @@ __global__ __launch_bounds__(NW * 64) void linear_decode_kernel(
         acc[mb] = __builtin_amdgcn_mfma_i32_16x16x64_i8(__builtin_bit_cast(v4i, a[mb][u]),
                                                         __builtin_bit_cast(v4i, b[u]), acc[mb], 0, 0, 0);
   }
+  if (w >= nss && w < MB) prefetch_epilogue();  // (K < 256 NW: a wave without a slice)
   __syncthreads();  // the zeroed sums are in place
 #pragma unroll
   for (int mb = 0; mb < MB; ++mb)
@@ -1006,17 +1048,21 @@ __global__ __launch_bounds__(NW * 64) void linear_decode_kernel(
   // 16x16 accumulator layout: lane holds column lane % 16, rows 4 * (lane / 16) + r
   // of its block of 16 tokens.
   const int n_idx = *n_idx_p;
-  const int64_t col = n0 + (lane & 15);
   if (col >= N) return;
-  const float scb = SCB[col];
-  const float bv = (bias != nullptr) ? to_f32<DT>(bias[col]) : 0.0f;
-  // Outlier columns eight at a time: a group's loads all go out before any
-  // of its arithmetic (indices clamped into range and the surplus products
-  // zeroed, rather than loads behind conditions or next to the division's
-  // branch, which the compiler waits on), then the products are added in
-  // column order.
+  // Outlier columns in groups of eight, products added in column order; the
+  // first group from the registers filled above, the others with all of a
+  // group's loads out before any of its arithmetic (indices clamped into
+  // range, surplus products zeroed: loads behind conditions or next to the
+  // division's branch are waited on one by one).
   float o[4] = {0.0f, 0.0f, 0.0f, 0.0f};
-  for (int p0 = 0; p0 < n_idx; p0 += 8) {
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    const float wv = to_f32<DT>(recover_w<DT>(cb0[j], scb));
+#pragma unroll
+    for (int r = 0; r < 4; ++r)
+      if (j < n_idx && tt[r] < T) o[r] += to_f32<DT>((xq0[r][j >> 1] >> (16 * (j & 1))) & 0xFFFFu) * wv;
+  }
+  for (int p0 = 8; p0 < n_idx; p0 += 8) {
     int8_t cb[8];
     uint16_t xb[8][4];
 #pragma unroll
@@ -1024,28 +1070,25 @@ __global__ __launch_bounds__(NW * 64) void linear_decode_kernel(
       const int p = p0 + j < n_idx ? p0 + j : n_idx - 1;
       cb[j] = CB[col * K + idx[p]];
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int t = 16 * mb + 4 * (lane >> 4) + r;
-        xb[j][r] = xo[((int64_t)(p >> 5) * T + (t < T ? t : T - 1)) * 32 + (p & 31)];
-      }
+      for (int r = 0; r < 4; ++r)
+        xb[j][r] = xo[((int64_t)(p >> 5) * T + (tt[r] < T ? tt[r] : T - 1)) * 32 + (p & 31)];
     }
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
       const bool okp = p0 + j < n_idx;
       const float wv = to_f32<DT>(recover_w<DT>(cb[j], scb));
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int t = 16 * mb + 4 * (lane >> 4) + r;
-        if (okp && t < T) o[r] += to_f32<DT>(xb[j][r]) * wv;
-      }
+      for (int r = 0; r < 4; ++r)
+        if (okp && tt[r] < T) o[r] += to_f32<DT>(xb[j][r]) * wv;
     }
   }
+  const float bv = to_f32<DT>(braw & bmask);
 #pragma unroll
   for (int r = 0; r < 4; ++r) {
-    const int t = 16 * mb + 4 * (lane >> 4) + r;
+    const int t = tt[r];
     if (t >= T) continue;
     if (acc_out != nullptr) acc_out[(int64_t)t * N + col] = sum[r];
-    const float d = (float)sum[r] * (SCA[t] * (scb * (1.0f / 16129.0f)));
+    const float d = (float)sum[r] * (sca[r] * (scb * (1.0f / 16129.0f)));
     out[(int64_t)t * N + col] = from_f32<DT>(d + o[r] + bv);
   }
 }
@@ -1098,12 +1141,12 @@ static hipError_t launch_linear_t(const LinearArgs& a, hipStream_t s) {
     // weight-streaming kernel: every weight row read once, N / 16 workgroups
     const int nb = (int)((a.N + 15) / 16);
     // 16 waves (one 256-byte slice each at K = 4096) while a wave's
-    // activation fragments fit in 128 registers, else 8
+    // fragments and prefetched epilogue operands fit in 128 registers, else 8
     decltype(&linear_decode_kernel<DT, 1, 16>) k = a.T <= 16 ? linear_decode_kernel<DT, 1, 16>
                                                   : a.T <= 32 ? linear_decode_kernel<DT, 2, 16>
-                                                  : a.T <= 64 ? linear_decode_kernel<DT, 4, 16>
+                                                  : a.T <= 64 ? linear_decode_kernel<DT, 4, 8>
                                                               : linear_decode_kernel<DT, 8, 8>;
-    k<<<dim3(nb), dim3(a.T <= 64 ? 16 * 64 : 8 * 64), 0, s>>>(
+    k<<<dim3(nb), dim3(a.T <= 32 ? 16 * 64 : 8 * 64), 0, s>>>(
         a.CA, a.CB, a.SCA, a.SCB, static_cast<const uint16_t*>(a.bias), static_cast<const uint16_t*>(a.xo),
         a.idx, a.n_idx, static_cast<uint16_t*>(a.out), a.acc, (int)a.T, (int)a.N, (int)a.K);
     return hipGetLastError();
