@@ -975,6 +975,9 @@ __global__ __launch_bounds__(NW * 64) void linear_decode_kernel(
   // columns the activation reads are out of their resource and return 0).
   // Wave w < MB requests those of token block w.
   const int mbe = w < MB ? w : MB - 1;
+  // (the outlier columns only where the registers allow: 16 waves hold at
+  // most 128 each)
+  constexpr bool PF_OUT = NW <= 8 || MB <= 2;
   const int64_t col = n0 + nr;
   const int64_t colc = col < N ? col : (int64_t)N - 1;
   const uint16_t* bsrc = (bias != nullptr) ? bias : reinterpret_cast<const uint16_t*>(SCB);
@@ -991,6 +994,7 @@ __global__ __launch_bounds__(NW * 64) void linear_decode_kernel(
     braw = bsrc[colc];
 #pragma unroll
     for (int r = 0; r < 4; ++r) sca[r] = SCA[tt[r] < T ? tt[r] : T - 1];
+    if constexpr (!PF_OUT) return;
 #pragma unroll
     for (int j = 0; j < 8; ++j) {  // idx holds K >= 16 entries
       const int c = idx[j];
@@ -1055,14 +1059,16 @@ __global__ __launch_bounds__(NW * 64) void linear_decode_kernel(
   // range, surplus products zeroed: loads behind conditions or next to the
   // division's branch are waited on one by one).
   float o[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+  if constexpr (PF_OUT) {
 #pragma unroll
-  for (int j = 0; j < 8; ++j) {
-    const float wv = to_f32<DT>(recover_w<DT>(cb0[j], scb));
+    for (int j = 0; j < 8; ++j) {
+      const float wv = to_f32<DT>(recover_w<DT>(cb0[j], scb));
 #pragma unroll
-    for (int r = 0; r < 4; ++r)
-      if (j < n_idx && tt[r] < T) o[r] += to_f32<DT>((xq0[r][j >> 1] >> (16 * (j & 1))) & 0xFFFFu) * wv;
+      for (int r = 0; r < 4; ++r)
+        if (j < n_idx && tt[r] < T) o[r] += to_f32<DT>((xq0[r][j >> 1] >> (16 * (j & 1))) & 0xFFFFu) * wv;
+    }
   }
-  for (int p0 = 8; p0 < n_idx; p0 += 8) {
+  for (int p0 = PF_OUT ? 8 : 0; p0 < n_idx; p0 += 8) {
     int8_t cb[8];
     uint16_t xb[8][4];
 #pragma unroll
