@@ -77,6 +77,8 @@ def kernel_bytes(name, case, n_idx):
         return 2 * T * K + T * K + 4 * T + 2 * T * npad + 4 * n_idx
     if name == "outlier_scan":
         return 2 * T * K
+    if name == "activation_split":  # scan and quantiser in one launch: X once, codes, list
+        return 2 * T * K + T * K + 4 * T + 2 * T * npad + 4 * n_idx + 4 * ((K + 31) // 32)
     if name == "quant_weight":
         return 2 * N * K + N * K + 4 * N
     if name == "decode_fused":  # the whole forward in one launch
@@ -99,6 +101,7 @@ def step_bytes(case):
 KERNEL_SOURCES = {
     "int8_gemm": "lli8_gemm.hip", "decode_fused": "lli8_decode.hip", "quant_activations": "lli8_quant.hip",
     "outlier_scan": "lli8_quant.hip", "quant_weight": "lli8_quant.hip", "bitmap_clear": "lli8_quant.hip",
+    "activation_split": "lli8_quant.hip",
     "recover_outliers": "lli8_quant.hip",
 }
 

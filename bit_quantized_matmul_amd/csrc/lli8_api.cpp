@@ -118,11 +118,19 @@ lli8_status_t enqueue_activation_split(const void* X, int64_t T, int64_t K, int 
                                        hipStream_t s) {
   const int64_t W = (K + 31) / 32;
   const bool scan = outliers_enabled(tau);
-  // the scan of a few rows writes every word itself; otherwise it ORs into a
-  // cleared bitmap, and with no scan the cleared bitmap is the result
-  if (!scan || !lli8::scan_writes_all_words(T, K)) TRACED(s, "bitmap_clear", lli8::launch_fill_u32(bitmap, W, 0u, s));
-  if (scan) TRACED(s, "outlier_scan", lli8::launch_scan_outliers(dt, X, T, K, tau, bitmap, s));
-  TRACED(s, "quant_activations", lli8::launch_quant_act(dt, X, T, K, bitmap, CA, SCA, idx, n_idx, xo, s));
+  if (lli8::split_small_supported(T, K)) {
+    // a few rows: scan and quantiser in one launch (a disabled threshold
+    // flags no column)
+    TRACED(s, "activation_split",
+           lli8::launch_split_small(dt, X, T, K, scan ? tau : 0.0f, CA, SCA, bitmap, idx, n_idx, xo, s));
+  } else {
+    // the scan of a few rows writes every word itself; otherwise it ORs into
+    // a cleared bitmap, and with no scan the cleared bitmap is the result
+    if (!scan || !lli8::scan_writes_all_words(T, K))
+      TRACED(s, "bitmap_clear", lli8::launch_fill_u32(bitmap, W, 0u, s));
+    if (scan) TRACED(s, "outlier_scan", lli8::launch_scan_outliers(dt, X, T, K, tau, bitmap, s));
+    TRACED(s, "quant_activations", lli8::launch_quant_act(dt, X, T, K, bitmap, CA, SCA, idx, n_idx, xo, s));
+  }
   if (wo != nullptr)
     TRACED(s, "recover_outliers", lli8::launch_recover_outliers(dt, CB, SCB, N, K, idx, n_idx, wo, wo_chunks, s));
   return LLI8_OK;

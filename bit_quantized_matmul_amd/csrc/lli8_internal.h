@@ -19,6 +19,13 @@ hipError_t launch_scan_outliers(int dt, const void* X, int64_t T, int64_t K, flo
 // clearing beforehand; otherwise it ORs into a zeroed bitmap.
 bool scan_writes_all_words(int64_t T, int64_t K);
 
+// Outlier scan and activation quantiser in one launch for a few rows (T <=
+// 32, K % 8 == 0, K <= 4096): bitmap, CA, SCA, idx, n_idx and Xo as the two
+// launches below write them.
+bool split_small_supported(int64_t T, int64_t K);
+hipError_t launch_split_small(int dt, const void* X, int64_t T, int64_t K, float tau, int8_t* CA, float* SCA,
+                              uint32_t* bitmap, int32_t* idx, int32_t* n_idx, void* xo, hipStream_t s);
+
 hipError_t launch_quant_act(int dt, const void* X, int64_t T, int64_t K, const uint32_t* bitmap,
                             int8_t* CA, float* SCA, int32_t* idx, int32_t* n_idx, void* xo,
                             hipStream_t s);

@@ -442,6 +442,135 @@ hipError_t launch_quant_weight(int dt, const void* W, int64_t N, int64_t K, int8
   return launch_quant_rows_t<DT_BF16, false>(w, N, K, CB, SCB, nullptr, nullptr, nullptr, nullptr, s);
 }
 
+// ------------------------------------------ few rows: split in one launch ----
+// T <= 32, K % 8 == 0, K <= 4096: the outlier scan and the row quantiser in
+// one launch, with no workgroup waiting on another.  Workgroup r quantises
+// row r, and every workgroup reads all T rows to find the outlier columns
+// itself (at most 256 KiB of X, in L2 after the first touch).  Thread c owns
+// the 8-column chunk c: its ROWS loads (rows past T repeat row T - 1, which
+// changes no maximum) all go out at once, then the column maxima give its
+// flags; its own row's chunk is one of them.  The rest follows the row
+// quantiser: absmax of the kept values (exact packed 16-bit maxima), codes by
+// code_pair16, outlier columns gathered into Xo at their rank in the
+// ascending index list, and workgroup 0 writes the bitmap, list and count.
+constexpr int64_t SPLIT_SMALL_MAX_T = 32;
+
+template <int DT, int ROWS>
+__global__ __launch_bounds__(512) void split_small_kernel(
+    const uint16_t* __restrict__ X, int64_t T, int64_t K, float tau, int8_t* __restrict__ codes,
+    float* __restrict__ scales, uint32_t* __restrict__ bitmap, int32_t* __restrict__ idx,
+    int32_t* __restrict__ n_idx, uint16_t* __restrict__ xo) {
+  __shared__ uint32_t s_words[128], s_prefix[128], s_max[8];
+  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+  const int64_t row = blockIdx.x;
+  const int64_t nch = K >> 3, W = (K + 31) >> 5;
+  const int c = tid;
+  const bool cok = c < nch;
+  const u32x4* p = reinterpret_cast<const u32x4*>(X) + (cok ? c : 0);
+  u32x4 v[ROWS];
+#pragma unroll
+  for (int i = 0; i < ROWS; ++i) v[i] = p[(i < T ? i : T - 1) * nch];
+  uint32_t m[4] = {0u, 0u, 0u, 0u};
+#pragma unroll
+  for (int i = 0; i < ROWS; ++i)
+#pragma unroll
+    for (int d = 0; d < 4; ++d) m[d] = pk_max_u16(m[d], v[i][d] & 0x7FFF7FFFu);
+  const uint32_t f8 = cok ? flags8(m, magnitude_threshold<DT>(tau)) : 0u;
+  uint32_t wv = f8 << ((c & 3) * 8);
+  wv |= __shfl_xor(wv, 1, WAVE);
+  wv |= __shfl_xor(wv, 2, WAVE);
+  if ((c & 3) == 0 && cok) s_words[c >> 2] = wv;
+
+  // this row's chunk; chunks past the row end count as all-outlier (excluded)
+  u32x4 x = v[0];
+#pragma unroll
+  for (int i = 1; i < ROWS; ++i)
+    if (i == row) x = v[i];
+  const uint32_t ob = cok ? f8 : 0xFFu;
+  uint32_t mx = 0u;
+#pragma unroll
+  for (int d = 0; d < 4; ++d) {
+    const uint32_t keep = (((ob >> (2 * d)) & 1u) ? 0u : 0x7FFFu) | (((ob >> (2 * d + 1)) & 1u) ? 0u : 0x7FFF0000u);
+    mx = pk_max_u16(mx, x[d] & keep);
+  }
+  mx = max(mx & 0xFFFFu, mx >> 16);
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) mx = max(mx, (uint32_t)__shfl_xor((int)mx, off, WAVE));
+  if (lane == 0) s_max[wid] = mx;
+  __syncthreads();
+  if (wid == 0) {  // exclusive prefix count of outlier columns per word (W <= 128: two per lane)
+    const uint32_t w0 = (2 * lane < W) ? s_words[2 * lane] : 0u;
+    const uint32_t w1 = (2 * lane + 1 < W) ? s_words[2 * lane + 1] : 0u;
+    const int cnt = __popc(w0) + __popc(w1);
+    const int run = wave_incl_scan(cnt) - cnt;
+    if (2 * lane < W) s_prefix[2 * lane] = (uint32_t)run;
+    if (2 * lane + 1 < W) s_prefix[2 * lane + 1] = (uint32_t)(run + __popc(w0));
+  }
+  __syncthreads();
+  const int total = (int)(s_prefix[W - 1] + __popc(s_words[W - 1]));
+  uint32_t bm = s_max[0];
+#pragma unroll
+  for (int i = 1; i < 8; ++i) bm = max(bm, s_max[i]);
+  const float am = to_f32<DT>(bm);  // exact absmax of the row's kept values
+  const float sc = (am > 0.0f) ? 127.0f / am : 0.0f;
+  if (cok) {
+    u32x2 pk;
+    pk[0] = pack_codes16(code_pair16<DT>(x[0], sc), code_pair16<DT>(x[1], sc)) & ~byte_mask4(ob);
+    pk[1] = pack_codes16(code_pair16<DT>(x[2], sc), code_pair16<DT>(x[3], sc)) & ~byte_mask4(ob >> 4);
+    reinterpret_cast<u32x2*>(codes + row * K)[c] = pk;
+  }
+  if (xo != nullptr) {
+    uint32_t f = f8;
+    if (f != 0u) {
+      const uint32_t word = s_words[c >> 2];
+      const int base = (int)s_prefix[c >> 2];
+      while (f) {
+        const int e = __builtin_ctz(f);
+        f &= f - 1u;
+        const int bit = (c & 3) * 8 + e;
+        const int rank = base + __popc(word & ((1u << bit) - 1u));
+        xo[xo_offset(rank, row, T)] = (uint16_t)half_bits(x, e);
+      }
+    }
+    if (wid == 0) xo_zero_pad(xo, total, row, T, lane);
+  }
+  if (tid == 0) scales[row] = am;
+  if (blockIdx.x == 0) {
+    for (int64_t w = tid; w < W; w += 512) {
+      const uint32_t word = s_words[w];
+      bitmap[w] = word;
+      uint32_t mm = word;
+      int pos = (int)s_prefix[w];
+      while (mm) {
+        const int b = __builtin_ctz(mm);
+        idx[pos++] = (int32_t)(w * 32 + b);
+        mm &= mm - 1u;
+      }
+    }
+    if (tid == 0) *n_idx = total;
+  }
+}
+
+bool split_small_supported(int64_t T, int64_t K) {
+  return T >= 1 && T <= SPLIT_SMALL_MAX_T && (K & 7) == 0 && K <= 4096;
+}
+
+hipError_t launch_split_small(int dt, const void* X, int64_t T, int64_t K, float tau, int8_t* CA, float* SCA,
+                              uint32_t* bitmap, int32_t* idx, int32_t* n_idx, void* xo, hipStream_t s) {
+  if (!split_small_supported(T, K)) return hipErrorInvalidValue;
+  const uint16_t* x = static_cast<const uint16_t*>(X);
+  uint16_t* g = static_cast<uint16_t*>(xo);
+  decltype(&split_small_kernel<DT_F16, 8>) k;
+  if (dt == DT_F16)
+    k = T <= 8 ? split_small_kernel<DT_F16, 8> : T <= 16 ? split_small_kernel<DT_F16, 16>
+      : T <= 24 ? split_small_kernel<DT_F16, 24> : split_small_kernel<DT_F16, 32>;
+  else
+    k = T <= 8 ? split_small_kernel<DT_BF16, 8> : T <= 16 ? split_small_kernel<DT_BF16, 16>
+      : T <= 24 ? split_small_kernel<DT_BF16, 24> : split_small_kernel<DT_BF16, 32>;
+  k<<<dim3((unsigned)T), dim3(512), 0, s>>>(x, T, K, tau, CA, SCA, bitmap, idx, n_idx, g);
+  return hipGetLastError();
+}
+
 hipError_t launch_quant_act(int dt, const void* X, int64_t T, int64_t K, const uint32_t* bitmap,
                             int8_t* CA, float* SCA, int32_t* idx, int32_t* n_idx, void* xo,
                             hipStream_t s) {

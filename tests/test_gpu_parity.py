@@ -381,3 +381,41 @@ def _sweep_case(seed):
 def test_random_sweep(seed):
     case, tau = _sweep_case(seed)
     _check_full(case, tau)
+
+
+# Few rows (T <= 32, K % 8 == 0, K <= 4096): the scan and the quantiser run
+# as one launch; each register depth (8, 16, 24, 32 rows), K not a multiple
+# of 16 or 32, either dtype, thresholds that flag nothing.
+SPLIT_SMALL = [(1, 8, 5, "f16", 6.0), (7, 40, 33, "bf16", 6.0), (8, 4096, 64, "f16", 6.0),
+               (12, 1000, 70, "f16", 2.5), (17, 4088, 100, "bf16", 6.0), (24, 4096, 300, "f16", 6.0),
+               (25, 520, 48, "bf16", 0.0), (32, 4096, 256, "f16", 6.0), (32, 2056, 40, "bf16", float("inf")),
+               (31, 96, 17, "f16", 1.0)]
+
+
+@pytest.mark.parametrize("T,K,N,dtype,tau", SPLIT_SMALL)
+def test_few_rows_one_launch_split(T, K, N, dtype, tau, monkeypatch):
+    """Outputs of the one-launch split (also with the fused decode off, so T <= 16
+    takes it inside lli8_int8_linear) and the gathered outlier columns it leaves
+    in scratch ([chunk][T][32], zero past n) against the oracle."""
+    B = _lib()
+    import torch
+    monkeypatch.setenv("LLI8_FUSED_DECODE", "0")
+    case = random_case(T, K, N, dtype=dtype, seed=500 + T + K, n_out=min(6, K))
+    g, r = _check_full(case, tau)
+    CA, SCA, bitmap, idx, n_idx = B.lli8_quant_rowwise_outliers(to_dev(case.X, dtype), tau)
+    n = int(n_idx.item())
+    assert n == r["idx"].size
+    assert np.array_equal(idx[:n].cpu().numpy(), r["idx"])
+    assert np.array_equal(CA.cpu().numpy(), r["CA"])
+    assert np.array_equal(SCA.cpu().numpy(), r["SCA"])
+    assert np.array_equal(bitmap.cpu().numpy().view(np.uint32), O.outlier_bitmap(r["idx"], K))
+    if n > 0:
+        X = to_dev(case.X, dtype)
+        CB, SCB = B.lli8_quant_weight_rowwise(to_dev(case.W, dtype))
+        _, ws = B.lli8_int8_linear(X, CB, SCB, None, tau)
+        torch.cuda.synchronize()
+        chunks = (n + 31) // 32
+        xo = ws.scratch[:chunks * T * 64].cpu().numpy().view(np.uint16).reshape(chunks, T, 32)
+        got = xo.transpose(1, 0, 2).reshape(T, chunks * 32)
+        assert np.array_equal(got[:, :n], case.X[:, r["idx"]])
+        assert not got[:, n:].any()
