@@ -447,9 +447,10 @@ hipError_t launch_quant_weight(int dt, const void* W, int64_t N, int64_t K, int8
 // one launch, with no workgroup waiting on another.  Workgroup r quantises
 // row r, and every workgroup reads all T rows to find the outlier columns
 // itself (at most 256 KiB of X, in L2 after the first touch).  Thread c owns
-// the 8-column chunk c: its ROWS loads (rows past T repeat row T - 1, which
-// changes no maximum) all go out at once, then the column maxima give its
-// flags; its own row's chunk is one of them.  The rest follows the row
+// the 8-column chunk c: its loads of all rows (rows past T repeat row T - 1,
+// which changes no maximum) go out at once, then the column maxima give its
+// flags; its own row's chunk is one of them.  (Two batches of 32 rows for T
+// up to 64 measured no faster than the two launches.)  The rest follows the row
 // quantiser: absmax of the kept values (exact packed 16-bit maxima), codes by
 // code_pair16, outlier columns gathered into Xo at their rank in the
 // ascending index list, and workgroup 0 writes the bitmap, list and count.
@@ -467,25 +468,28 @@ __global__ __launch_bounds__(512) void split_small_kernel(
   const int c = tid;
   const bool cok = c < nch;
   const u32x4* p = reinterpret_cast<const u32x4*>(X) + (cok ? c : 0);
-  u32x4 v[ROWS];
-#pragma unroll
-  for (int i = 0; i < ROWS; ++i) v[i] = p[(i < T ? i : T - 1) * nch];
   uint32_t m[4] = {0u, 0u, 0u, 0u};
+  u32x4 x = (u32x4){0u, 0u, 0u, 0u};  // this row's chunk
+  for (int r0 = 0; r0 < T; r0 += ROWS) {  // one batch (T <= ROWS)
+    u32x4 v[ROWS];
 #pragma unroll
-  for (int i = 0; i < ROWS; ++i)
+    for (int i = 0; i < ROWS; ++i) v[i] = p[(r0 + i < T ? r0 + i : T - 1) * nch];
+    __builtin_amdgcn_sched_barrier(0);  // the batch's loads all in flight before the first wait
 #pragma unroll
-    for (int d = 0; d < 4; ++d) m[d] = pk_max_u16(m[d], v[i][d] & 0x7FFF7FFFu);
+    for (int i = 0; i < ROWS; ++i)
+#pragma unroll
+      for (int d = 0; d < 4; ++d) m[d] = pk_max_u16(m[d], v[i][d] & 0x7FFF7FFFu);
+#pragma unroll
+    for (int i = 0; i < ROWS; ++i)
+      if (r0 + i == row) x = v[i];
+  }
   const uint32_t f8 = cok ? flags8(m, magnitude_threshold<DT>(tau)) : 0u;
   uint32_t wv = f8 << ((c & 3) * 8);
   wv |= __shfl_xor(wv, 1, WAVE);
   wv |= __shfl_xor(wv, 2, WAVE);
   if ((c & 3) == 0 && cok) s_words[c >> 2] = wv;
 
-  // this row's chunk; chunks past the row end count as all-outlier (excluded)
-  u32x4 x = v[0];
-#pragma unroll
-  for (int i = 1; i < ROWS; ++i)
-    if (i == row) x = v[i];
+  // chunks past the row end count as all-outlier (excluded)
   const uint32_t ob = cok ? f8 : 0xFFu;
   uint32_t mx = 0u;
 #pragma unroll

@@ -385,11 +385,13 @@ def test_random_sweep(seed):
 
 # Few rows (T <= 32, K % 8 == 0, K <= 4096): the scan and the quantiser run
 # as one launch; each register depth (8, 16, 24, 32 rows), K not a multiple
-# of 16 or 32, either dtype, thresholds that flag nothing.
+# of 16 or 32, either dtype, thresholds that flag nothing; and a few shapes
+# just past it, on the two-launch split.
 SPLIT_SMALL = [(1, 8, 5, "f16", 6.0), (7, 40, 33, "bf16", 6.0), (8, 4096, 64, "f16", 6.0),
                (12, 1000, 70, "f16", 2.5), (17, 4088, 100, "bf16", 6.0), (24, 4096, 300, "f16", 6.0),
                (25, 520, 48, "bf16", 0.0), (32, 4096, 256, "f16", 6.0), (32, 2056, 40, "bf16", float("inf")),
-               (31, 96, 17, "f16", 1.0)]
+               (31, 96, 17, "f16", 1.0), (33, 4096, 64, "f16", 6.0), (47, 1032, 20, "bf16", 6.0),
+               (64, 4096, 128, "f16", 6.0), (64, 8, 9, "bf16", 0.0)]
 
 
 @pytest.mark.parametrize("T,K,N,dtype,tau", SPLIT_SMALL)
