@@ -1009,32 +1009,41 @@ __global__ __launch_bounds__(NW * 64) void linear_decode_kernel(
       xq0[r] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rx, (tt[r] < T ? tt[r] : T - 1) * 64, 0, 0));
   };
 
-  for (int s = w; s < nss; s += NW) {
-    const int kb = s * 256 + g * 16;
-    u32x4 b[4];
+  // Slices per pass: two where the registers allow (a second slice past the
+  // end reads out of range, i.e. zeros), so that at K = 4096 each wave's
+  // loads all go out at once.
+  constexpr int SL = (MB == 4 && NW == 8) ? 2 : 1;
+  for (int s = w; s < nss; s += SL * NW) {
+    u32x4 b[SL][4];
+    u32x4 a[SL][MB][4];
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const int k = kb + 64 * u;
-      b[u] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rb, k < K ? nr * K + k : OOB, 0, 2));
-    }
-    u32x4 a[MB][4];
-#pragma unroll
-    for (int mb = 0; mb < MB; ++mb)
+    for (int l = 0; l < SL; ++l) {
+      const int kb = (s + l * NW) * 256 + g * 16;
 #pragma unroll
       for (int u = 0; u < 4; ++u) {
         const int k = kb + 64 * u;
-        a[mb][u] = __builtin_bit_cast(
-            u32x4, __builtin_amdgcn_raw_buffer_load_b128(ra, k < K ? (16 * mb + nr) * K + k : OOB, 0, 0));
+        b[l][u] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rb, k < K ? nr * K + k : OOB, 0, 2));
       }
+#pragma unroll
+      for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          const int k = kb + 64 * u;
+          a[l][mb][u] = __builtin_bit_cast(
+              u32x4, __builtin_amdgcn_raw_buffer_load_b128(ra, k < K ? (16 * mb + nr) * K + k : OOB, 0, 0));
+        }
+    }
     if (s == w && w < MB) prefetch_epilogue();
-    // every load of the slice in flight before the first MFMA waits for one
+    // every load of the pass in flight before the first MFMA waits for one
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-    for (int mb = 0; mb < MB; ++mb)
+    for (int l = 0; l < SL; ++l)
 #pragma unroll
-      for (int u = 0; u < 4; ++u)
-        acc[mb] = __builtin_amdgcn_mfma_i32_16x16x64_i8(__builtin_bit_cast(v4i, a[mb][u]),
-                                                        __builtin_bit_cast(v4i, b[u]), acc[mb], 0, 0, 0);
+      for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+        for (int u = 0; u < 4; ++u)
+          acc[mb] = __builtin_amdgcn_mfma_i32_16x16x64_i8(__builtin_bit_cast(v4i, a[l][mb][u]),
+                                                          __builtin_bit_cast(v4i, b[l][u]), acc[mb], 0, 0, 0);
   }
   if (w >= nss && w < MB) prefetch_epilogue();  // (K < 256 NW: a wave without a slice)
   __syncthreads();  // the zeroed sums are in place
