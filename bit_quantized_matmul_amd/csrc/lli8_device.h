@@ -44,6 +44,17 @@ __device__ __forceinline__ uint16_t from_f32(float v) {
 // the IEEE division (checked on the device against the division for every
 // float in that range, both signs); other values (tiny, huge, inf, NaN) take
 // the division itself.
+// The multiply-and-correct form alone, for callers that know p is in
+// range: p = fl32(c * s) with |c| <= 127 an integer and 2^-93 <= s < 2^94
+// (div127_scale_ok) lies in it, or is zero.
+__device__ __forceinline__ float div127_inrange(float p) {
+  constexpr float r = 1.0f / 127.0f;
+  const float q0 = p * r;
+  const float e = __builtin_fmaf(-q0, 127.0f, p);  // exact remainder
+  return __builtin_fmaf(e, r, q0);
+}
+__device__ __forceinline__ bool div127_scale_ok(float s) { return s >= 0x1p-93f && s < 0x1p94f; }
+
 __device__ __forceinline__ float div127(float p) {
   constexpr float r = 1.0f / 127.0f;
   const float a = __builtin_fabsf(p);

@@ -624,11 +624,21 @@ __global__ __launch_bounds__(256) void recover_outliers_kernel(
       const uint32_t d0 = src[0], d1 = src[1], d2 = (sh != 0) ? src[2] : 0u;
       const uint32_t lo = (uint32_t)(((uint64_t)d1 << 32 | d0) >> (8 * sh));
       const uint32_t hi = (uint32_t)(((uint64_t)d2 << 32 | d1) >> (8 * sh));
+      // the division's range test once per piece, not per value (the eight
+      // values share the row scale): the conversion and division are most of
+      // this kernel's work when every column is an outlier
+      if (div127_scale_ok(scb)) {
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const int8_t cb = (int8_t)(((e < 4 ? lo : hi) >> (8 * (e & 3))) & 0xFFu);
-        const uint32_t w = from_f32<DT>(div127((float)cb * scb));
-        v[e >> 1] |= w << (16 * (e & 1));
+        for (int e = 0; e < 8; ++e) {
+          const int8_t cb = (int8_t)(((e < 4 ? lo : hi) >> (8 * (e & 3))) & 0xFFu);
+          v[e >> 1] |= (uint32_t)from_f32<DT>(div127_inrange((float)cb * scb)) << (16 * (e & 1));
+        }
+      } else {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const int8_t cb = (int8_t)(((e < 4 ? lo : hi) >> (8 * (e & 3))) & 0xFFu);
+          v[e >> 1] |= (uint32_t)from_f32<DT>(div127((float)cb * scb)) << (16 * (e & 1));
+        }
       }
     } else {
 #pragma unroll

@@ -319,13 +319,16 @@ def test_many_outlier_chunks_large_tiles(T, K, N, n_out, tau, dtype):
     assert g["n"] >= min(n_out, K) and (tau > 0.1 or g["n"] == K)
 
 
+@pytest.mark.parametrize("every_column", [False, True])
 @pytest.mark.parametrize("dtype", ["f16", "bf16"])
-def test_recovered_weights_bit_exact(dtype):
+def test_recovered_weights_bit_exact(dtype, every_column):
     """The recovered outlier weights the tile path writes to scratch (chunk-major
     [chunk][N][32], zero past n) equal the oracle's dtype(fl32(fl32(CB * SCB) /
     127)) bit for bit.  For bf16 some weight rows are scaled far down or up, so
     that products below 2^-100 and above 2^101 take the full division and the
-    rest the multiply-and-correct form."""
+    rest the multiply-and-correct form.  With every column an outlier (a tiny
+    threshold) the pieces are runs of consecutive columns, whose row-scale
+    range test is taken once per piece."""
     B = _lib()
     import torch
     T, K, N = 256, 512, 300
@@ -337,10 +340,11 @@ def test_recovered_weights_bit_exact(dtype):
         vals[3::11] *= 1e34
         Wb = O.round_to_dtype_bits(vals, dtype)
     CB, SCB = B.lli8_quant_weight_rowwise(to_dev(Wb, dtype))
-    _, ws = B.lli8_int8_linear(to_dev(case.X, dtype), CB, SCB, None, 6.0)
+    tau = 1e-30 if every_column else 6.0
+    _, ws = B.lli8_int8_linear(to_dev(case.X, dtype), CB, SCB, None, tau)
     torch.cuda.synchronize()
     n = int(ws.n_idx.item())
-    assert n >= 40
+    assert n == K if every_column else n >= 40
     idx = ws.idx[:n].cpu().numpy()
     chunks = (n + 31) // 32
     xb = T * ((K + 31) // 32 * 32) * 2
