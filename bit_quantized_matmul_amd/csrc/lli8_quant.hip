@@ -641,10 +641,20 @@ __global__ __launch_bounds__(256) void recover_outliers_kernel(
         }
       }
     } else {
+      // scattered columns: the eight indices, then the eight bytes, each set
+      // requested at once (index clamped into the list; surplus values are
+      // dropped below), rather than a load behind a condition per value,
+      // which the compiler waits on one at a time
+      int col[8];
+      int8_t cbv[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) col[e] = idx[p0 + e < total ? p0 + e : total - 1];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) cbv[e] = cbrow[col[e]];
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
         if (p0 + e < total) {
-          const uint32_t w = from_f32<DT>(div127((float)cbrow[idx[p0 + e]] * scb));
+          const uint32_t w = from_f32<DT>(div127((float)cbv[e] * scb));
           v[e >> 1] |= w << (16 * (e & 1));
         }
       }
