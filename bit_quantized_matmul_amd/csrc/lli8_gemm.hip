@@ -417,6 +417,9 @@ __device__ __forceinline__ void tile_epilogue(
 // DL = D >= 3 (K % BK == 0): straight into a D-slot LDS ring, D - 1 steps ahead.
 // FL = 1: every tile lies wholly inside the output (T % BM == 0, N % BN ==
 // 0, N even), and the epilogue drops its bounds checks.
+// KM (register-staged loads): 0 K % BK == 0; 1 K % 16 == 0 (16-byte loads,
+// chunks past K zeroed); 3 K % 8 == 0 (8-byte loads); 4 K % 4 == 0 (4-byte
+// loads); 2 any K (bytes).
 template <int DT, int BM, int BN, int KM, int BK, int WGM, int WGN, int GM, int DL, int FL>
 __global__ __launch_bounds__(64 * WGM * WGN) void linear_tile_kernel(
     const int8_t* __restrict__ CA, const int8_t* __restrict__ CB, const float* __restrict__ SCA,
@@ -483,13 +486,34 @@ __global__ __launch_bounds__(64 * WGM * WGN) void linear_tile_kernel(
   const int cq = (tid % CPR) * 16;  // byte offset of this thread's chunk within a step
   u32x4 ra0[LA], rb0[LB], ra1[LA], rb1[LB];
   auto ld = [&](const int8_t* row, int k) -> u32x4 {
-    if constexpr (KM == 2) {  // K % 16 != 0: byte-wise, zero past K
+    // Narrow loads past K read an in-range address and are zeroed after the
+    // load: a load behind the condition would be a branch, and the compiler
+    // waits for every load in flight before each one (16x slower at K = 4008).
+    if constexpr (KM == 2) {  // K % 4 != 0: byte-wise, zero past K
       uint32_t wv[4] = {0u, 0u, 0u, 0u};
 #pragma unroll
       for (int bb = 0; bb < 16; ++bb) {
         const int kk = k + bb;
-        const uint32_t v = (kk < K) ? (uint32_t)(uint8_t)row[kk] : 0u;
-        wv[bb >> 2] |= v << (8 * (bb & 3));
+        const uint32_t v = (uint32_t)(uint8_t)row[kk < K ? kk : 0];
+        wv[bb >> 2] |= (kk < K ? v : 0u) << (8 * (bb & 3));
+      }
+      return (u32x4){wv[0], wv[1], wv[2], wv[3]};
+    } else if constexpr (KM == 3) {  // K % 8 == 0, K % 16 != 0: two 8-byte halves
+      u32x2 h[2];
+#pragma unroll
+      for (int d = 0; d < 2; ++d) {
+        const int kd = k + 8 * d;
+        const u32x2 v = *reinterpret_cast<const u32x2*>(row + (kd < K ? kd : 0));
+        h[d] = kd < K ? v : (u32x2){0u, 0u};
+      }
+      return (u32x4){h[0][0], h[0][1], h[1][0], h[1][1]};
+    } else if constexpr (KM == 4) {  // K % 4 == 0, K % 8 != 0: dword-wise
+      uint32_t wv[4];
+#pragma unroll
+      for (int d = 0; d < 4; ++d) {
+        const int kd = k + 4 * d;
+        const uint32_t v = *reinterpret_cast<const uint32_t*>(row + (kd < K ? kd : 0));
+        wv[d] = kd < K ? v : 0u;
       }
       return (u32x4){wv[0], wv[1], wv[2], wv[3]};
     } else {
@@ -1124,6 +1148,8 @@ static hipError_t launch_tile(const LinearArgs& a, hipStream_t s) {
     k = (a.K % BK) == 0 ? (full ? linear_tile_kernel<DT, BM, BN, 0, BK, WGM, WGN, GM, 0, 1>
                                 : linear_tile_kernel<DT, BM, BN, 0, BK, WGM, WGN, GM, 0, 0>)
         : (a.K % 16) == 0 ? linear_tile_kernel<DT, BM, BN, 1, BK, WGM, WGN, GM, 0, 0>
+        : (a.K % 8) == 0  ? linear_tile_kernel<DT, BM, BN, 3, BK, WGM, WGN, GM, 0, 0>
+        : (a.K % 4) == 0  ? linear_tile_kernel<DT, BM, BN, 4, BK, WGM, WGN, GM, 0, 0>
                           : linear_tile_kernel<DT, BM, BN, 2, BK, WGM, WGN, GM, 0, 0>;
   }
   k<<<dim3(nb), dim3(64 * WGM * WGN), 0, s>>>(a.CA, a.CB, a.SCA, a.SCB, static_cast<const uint16_t*>(a.bias),
