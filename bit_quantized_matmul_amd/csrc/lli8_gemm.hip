@@ -1215,8 +1215,12 @@ static hipError_t launch_linear_t(const LinearArgs& a, hipStream_t s) {
   }
   // 128 x 128 tiles unless they leave most of the chip idle; then 64 x 64
   const int64_t t128 = ((a.T + 127) / 128) * ((a.N + 127) / 128);
-  if (t128 < 256) return launch_tile<DT, 64, 64, 64, 2, 2>(a, s);
-  return launch_tile<DT, 128, 128, 64, 2, 2>(a, s);
+  // (both take K straight into a 4-slot LDS ring when K % 64 == 0: three
+  // steps in flight rather than two register sets; 64 x 64 at T = 129-256,
+  // K = N = 4096: 40 -> 31-33 us)
+  if (t128 < 256)
+    return (a.K % 64) == 0 ? launch_tile<DT, 64, 64, 64, 2, 2, 8, 4>(a, s) : launch_tile<DT, 64, 64, 64, 2, 2>(a, s);
+  return (a.K % 64) == 0 ? launch_tile<DT, 128, 128, 64, 2, 2, 8, 4>(a, s) : launch_tile<DT, 128, 128, 64, 2, 2>(a, s);
 }
 
 hipError_t launch_linear_gemm(const LinearArgs& a, hipStream_t s) {
