@@ -1192,12 +1192,19 @@ static hipError_t launch_linear_t(const LinearArgs& a, hipStream_t s) {
         a.idx, a.n_idx, static_cast<uint16_t*>(a.out), a.acc, (int)a.T, (int)a.N, (int)a.K);
     return hipGetLastError();
   }
-  if (a.T >= 512 && a.N >= 512 && a.K < (1 << 24)) {
+  // 256 x 256 tiles once there are enough of them to fill half the chip;
+  // with fewer, smaller tiles finish sooner (T = 512-1024, N = K = 4096:
+  // 46-47 -> 22-30 us; T = 512, N = 11008: 46.8 -> 41.3 us; from 129 tiles of
+  // 256 x 256 on, those win)
+  int cus = 0;
+  {
+    const hipError_t e = compute_units(cus);
+    if (e != hipSuccess) return e;
+  }
+  const int64_t t256 = ((a.T + 255) / 256) * ((a.N + 255) / 256);
+  if (a.T >= 512 && a.N >= 512 && a.K < (1 << 24) && 2 * t256 >= cus) {
     // whole 256 x 256 tiles: one workgroup per compute unit walks its tiles
     if (a.T % 256 == 0 && a.N % 256 == 0 && a.K % 256 == 0) {
-      int cus = 0;
-      const hipError_t e = compute_units(cus);
-      if (e != hipSuccess) return e;
       const int tiles_m = (int)(a.T / 256), tiles_n = (int)(a.N / 256);
       const int nb = tiles_m * tiles_n;
       const int G = nb < cus ? nb : cus;

@@ -65,10 +65,12 @@ SHAPES = [
     (1, 64, 64), (3, 24, 5), (8, 8, 4), (16, 4096, 130), (17, 520, 300), (33, 136, 65),
     (100, 264, 257), (130, 1000, 129), (257, 512, 513), (300, 136, 40), (64, 8, 1), (5, 100, 7),
     (2, 17, 3), (40, 37, 11), (600, 640, 520),
-    # large tiles: 128-byte steps in pairs (K % 256 == 0; two steps only at
-    # K = 256), 64-byte steps (K % 64 == 0), register staging (other K), each
-    # with ragged T and N tails
+    # T, N >= 512 with fewer than 128 tiles of 256 x 256: small tiles
     (600, 768, 520), (513, 256, 777), (512, 512, 512), (530, 520, 515), (515, 100, 520),
+    # large tiles (at least 128 of them): 128-byte steps in pairs (K % 256 ==
+    # 0; two steps only at K = 256), 64-byte steps (K % 64 == 0), register
+    # staging (8-byte, 4-byte loads), each with ragged T and N tails
+    (2000, 768, 4100), (2050, 256, 4097), (2048, 576, 4096), (2000, 520, 4100), (2001, 100, 4100),
     # 16 < T <= 128 with K % 16 == 0: the weight-streaming kernel, 2, 4 or 8 token blocks
     (17, 512, 300), (32, 4096, 520), (33, 256, 65), (48, 2048, 1000), (64, 1024, 130),
     (65, 512, 100), (128, 4096, 260), (100, 1040, 33),
@@ -312,6 +314,8 @@ def test_persistent_tiles(T, K, N, n_out, tau, dtype):
     (600, 512, 520, 150, 6.0),    # 5 outlier chunks: 4 through the 2-slot pipeline, 1 through the ring
     (520, 768, 530, 0, 0.01),     # every column an outlier: 24 chunks, all through the pipeline
     (512, 1024, 512, 260, 6.0),   # 9 chunks: 8 + 1
+    # the same on 256 x 256 tiles (at least 128 of them)
+    (2000, 512, 4100, 150, 6.0), (2000, 768, 4100, 0, 0.01), (2000, 1024, 4100, 260, 6.0),
 ])
 def test_many_outlier_chunks_large_tiles(T, K, N, n_out, tau, dtype):
     case = random_case(T, K, N, dtype=dtype, seed=T + K + n_out, n_out=n_out)
