@@ -1224,9 +1224,12 @@ static hipError_t launch_linear_t(const LinearArgs& a, hipStream_t s) {
   const int64_t t128 = ((a.T + 127) / 128) * ((a.N + 127) / 128);
   // (both take K straight into a 4-slot LDS ring when K % 64 == 0: three
   // steps in flight rather than two register sets; 64 x 64 at T = 129-256,
-  // K = N = 4096: 40 -> 31-33 us)
+  // K = N = 4096: 40 -> 31-33 us, and with 128-byte steps when K % 128 == 0
+  // 27-29 us)
   if (t128 < 256)
-    return (a.K % 64) == 0 ? launch_tile<DT, 64, 64, 64, 2, 2, 8, 4>(a, s) : launch_tile<DT, 64, 64, 64, 2, 2>(a, s);
+    return (a.K % 128) == 0 ? launch_tile<DT, 64, 64, 128, 2, 2, 8, 4>(a, s)
+           : (a.K % 64) == 0 ? launch_tile<DT, 64, 64, 64, 2, 2, 8, 4>(a, s)
+                             : launch_tile<DT, 64, 64, 64, 2, 2>(a, s);
   return (a.K % 64) == 0 ? launch_tile<DT, 128, 128, 64, 2, 2, 8, 4>(a, s) : launch_tile<DT, 128, 128, 64, 2, 2>(a, s);
 }
 
