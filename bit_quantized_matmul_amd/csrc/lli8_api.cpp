@@ -301,7 +301,7 @@ lli8_status_t lli8_int8_linear(const void* X, int64_t T, int64_t K, int64_t N, l
   // only: the weight-streaming kernel reads CB itself)
   void* wo = nullptr;
   int wo_chunks = 0;
-  if (outl && (T > lli8::LLI8_STREAM_MAX_T || (K % 16) != 0)) {
+  if (outl && !lli8::stream_gemm_route(T, N, K)) {
     const size_t xb = xo_bytes(T, K), per_chunk = (size_t)N * 64;
     const size_t room = ws->scratch_bytes > xb ? ws->scratch_bytes - xb : 0;
     const int64_t c = (int64_t)(room / per_chunk), cmax = (K + 31) / 32;

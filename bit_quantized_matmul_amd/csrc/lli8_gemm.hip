@@ -24,9 +24,9 @@
 //     place (same 32x32 register layout), runs the outlier columns through
 //     v_mfma_f32_32x32x16_{f16,bf16} on the same registers, then adds the
 //     bias and rounds once to the output dtype.
-//   * weight-streaming kernel (T <= 128, K % 16 == 0): each workgroup owns
+//   * weight-streaming kernel (up to 64 tokens, K % 16 == 0): each workgroup owns
 //     16 output features and reads their int8 weight rows once with 16-byte
-//     loads, four waves splitting K, v_mfma_i32_16x16x64_i8 per block of 16
+//     loads, 8 or 16 waves splitting K, v_mfma_i32_16x16x64_i8 per block of 16
 //     tokens.
 #include "lli8_device.h"
 #include "lli8_internal.h"
@@ -951,7 +951,7 @@ __global__ __launch_bounds__(512) void linear_persist_kernel(
 }
 
 // ---------------------------------------------------------------- decode ----
-// T <= 16 MB, K % 16 == 0.  Workgroup = 16 output features in NW waves;
+// T <= 16 MB (MB <= 4), K % 16 == 0.  Workgroup = 16 output features in NW waves;
 // wave w takes the 256-byte K slices w, w + NW, ... and issues all of a
 // slice's loads before its first MFMA.  Lane (n, g) = (lane % 16, lane / 16)
 // loads bytes 16 g + 64 u .. + 15 (u = 0 .. 3) of the slice of weight row n
@@ -1178,15 +1178,14 @@ static hipError_t compute_units(int& cus) {
 
 template <int DT>
 static hipError_t launch_linear_t(const LinearArgs& a, hipStream_t s) {
-  if (a.T <= LLI8_STREAM_MAX_T && (a.K % 16) == 0) {
+  if (stream_gemm_route(a.T, a.N, a.K)) {
     // weight-streaming kernel: every weight row read once, N / 16 workgroups
     const int nb = (int)((a.N + 15) / 16);
     // 16 waves (one 256-byte slice each at K = 4096) while a wave's
     // fragments and prefetched epilogue operands fit in 128 registers, else 8
     decltype(&linear_decode_kernel<DT, 1, 16>) k = a.T <= 16 ? linear_decode_kernel<DT, 1, 16>
                                                   : a.T <= 32 ? linear_decode_kernel<DT, 2, 16>
-                                                  : a.T <= 64 ? linear_decode_kernel<DT, 4, 8>
-                                                              : linear_decode_kernel<DT, 8, 8>;
+                                                              : linear_decode_kernel<DT, 4, 8>;
     k<<<dim3(nb), dim3(a.T <= 32 ? 16 * 64 : 8 * 64), 0, s>>>(
         a.CA, a.CB, a.SCA, a.SCB, static_cast<const uint16_t*>(a.bias), static_cast<const uint16_t*>(a.xo),
         a.idx, a.n_idx, static_cast<uint16_t*>(a.out), a.acc, (int)a.T, (int)a.N, (int)a.K);

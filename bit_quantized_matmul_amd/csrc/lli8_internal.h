@@ -32,9 +32,16 @@ hipError_t launch_quant_act(int dt, const void* X, int64_t T, int64_t K, const u
 
 // Recovered weights of the first min(ceil(n/32), chunks) outlier chunks,
 // chunk-major [chunk][N][32] 16-bit (n read on the device).
-// Largest T the weight-streaming GEMM kernel takes (K % 16 == 0); above it
-// the tile kernel runs and reads recovered outlier weights from scratch.
-constexpr int64_t LLI8_STREAM_MAX_T = 128;
+// Whether the weight-streaming GEMM kernel takes a shape (K % 16 == 0): it
+// reads each weight row once but every workgroup reads all of CA, so it
+// wins for up to 32 tokens, and up to 64 on layers of at most 4096 x 4096
+// (T = 48: 21 against 26 us there; at N = 11008 the tiles take 13 against
+// 37 us, at K = 12288 24 against 31 us; T = 65-128 on tiles 26-27 against
+// 27-32 us).  Otherwise the tile kernels run and read recovered outlier
+// weights from scratch.
+inline bool stream_gemm_route(int64_t T, int64_t N, int64_t K) {
+  return (K % 16) == 0 && (T <= 32 || (T <= 64 && N * K <= (int64_t)4096 * 4096));
+}
 
 hipError_t launch_quant_vectorwise(int dt, const void* X, int64_t R, int64_t C, int zeropoint, int axis,
                                    int8_t* codes, float* scale, int32_t* zp, hipStream_t s);
