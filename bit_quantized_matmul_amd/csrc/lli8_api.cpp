@@ -301,7 +301,10 @@ lli8_status_t lli8_int8_linear(const void* X, int64_t T, int64_t K, int64_t N, l
   // only: the weight-streaming kernel reads CB itself)
   void* wo = nullptr;
   int wo_chunks = 0;
-  if (outl && !lli8::stream_gemm_route(T, N, K)) {
+  // (up to 256 tokens the tiles gather CB at the outlier columns themselves:
+  // fewer tile rows read each weight row, and the launch saved is worth more,
+  // T = 65-256 at N = K = 4096: 26.3-28.4 -> 25.1-26.6 us)
+  if (outl && !lli8::stream_gemm_route(T, N, K) && T > 256) {
     const size_t xb = xo_bytes(T, K), per_chunk = (size_t)N * 64;
     const size_t room = ws->scratch_bytes > xb ? ws->scratch_bytes - xb : 0;
     const int64_t c = (int64_t)(room / per_chunk), cmax = (K + 31) / 32;

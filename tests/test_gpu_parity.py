@@ -336,7 +336,7 @@ def test_recovered_weights_bit_exact(dtype, every_column):
     range test is taken once per piece."""
     B = _lib()
     import torch
-    T, K, N = 256, 512, 300
+    T, K, N = 512, 512, 300  # past 256 tokens the recovery runs before the tiles
     case = random_case(T, K, N, dtype=dtype, seed=77, n_out=40)
     Wb = case.W
     if dtype == "bf16":
