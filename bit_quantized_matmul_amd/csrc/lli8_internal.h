@@ -34,13 +34,15 @@ hipError_t launch_quant_act(int dt, const void* X, int64_t T, int64_t K, const u
 // chunk-major [chunk][N][32] 16-bit (n read on the device).
 // Whether the weight-streaming GEMM kernel takes a shape (K % 16 == 0): it
 // reads each weight row once but every workgroup reads all of CA, so it
-// wins for up to 32 tokens, and up to 64 on layers of at most 4096 x 4096
-// (T = 48: 21 against 26 us there; at N = 11008 the tiles take 13 against
-// 37 us, at K = 12288 24 against 31 us; T = 65-128 on tiles 26-27 against
-// 27-32 us).  Otherwise the tile kernels run and read recovered outlier
-// weights from scratch.
+// wins only on layers of at most 4096 outputs, for up to 32 tokens at any
+// depth and up to 64 at K <= 4096 (GEMM times: T = 32, K = 12288: 23.5
+// against 27.7 us on tiles; T = 48, K = N = 4096: 21 against 26 us).  Wider
+// layers go to the tiles (T = 32, N = 11008: 16.4 against 27.8 us; N = 28672:
+// 25.7 against 61.1 us), and so do more tokens (T = 65-128: 26-27 against
+// 27-32 us for the step).  The tiles read recovered outlier weights from
+// scratch past 256 tokens and gather them from CB below that.
 inline bool stream_gemm_route(int64_t T, int64_t N, int64_t K) {
-  return (K % 16) == 0 && (T <= 32 || (T <= 64 && N * K <= (int64_t)4096 * 4096));
+  return (K % 16) == 0 && N <= 4096 && (T <= 32 || (T <= 64 && K <= 4096));
 }
 
 hipError_t launch_quant_vectorwise(int dt, const void* X, int64_t R, int64_t C, int zeropoint, int axis,

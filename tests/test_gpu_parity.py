@@ -71,8 +71,8 @@ SHAPES = [
     # 0; two steps only at K = 256), 64-byte steps (K % 64 == 0), register
     # staging (8-byte, 4-byte loads), each with ragged T and N tails
     (2000, 768, 4100), (2050, 256, 4097), (2048, 576, 4096), (2000, 520, 4100), (2001, 100, 4100),
-    # 16 < T <= 64 with K % 16 == 0 (T <= 32, or N K <= 4096^2): the weight-streaming
-    # kernel, 2 or 4 token blocks; past that the tiles
+    # 16 < T <= 64 with K % 16 == 0 and N <= 4096 (K <= 4096 past 32 tokens): the
+    # weight-streaming kernel, 2 or 4 token blocks; otherwise the tiles
     (17, 512, 300), (32, 4096, 520), (33, 256, 65), (48, 2048, 1000), (64, 1024, 130),
     (65, 512, 100), (128, 4096, 260), (100, 1040, 33),
     # T < 512 with at least 256 tiles of 128 x 128: the 128 x 128 tile path (others take 64 x 64)
