@@ -234,12 +234,6 @@ def zeropoint_quantize(X: np.ndarray, axis: int):
     return np.ascontiguousarray(codes.T), nd, zp
 
 
-def absmax_dequantize(codes: np.ndarray, amax: np.ndarray, axis: int) -> np.ndarray:
-    """x^ = code * absmax / 127 (float64)."""
-    a = amax.astype(np.float64) / INT8_MAX
-    return codes.astype(np.float64) * (a[:, None] if axis == 1 else a[None, :])
-
-
 def zeropoint_dequantize(codes: np.ndarray, nd: np.ndarray, zp: np.ndarray, axis: int) -> np.ndarray:
     """x^ = (code - zp) / nd (float64); 0 where nd = 0."""
     n = nd.astype(np.float64)
@@ -292,7 +286,10 @@ def linear_forward(X_bits, dtype, CB, SCB, bias_bits, threshold, rows=None, cols
     evaluate (the outlier set is always taken over every row of X).
 
     Returns a dict: idx, CA, SCA (selected rows), acc (selected block, int32),
-    out64 (float64, before the final rounding) and out_bits (uint16).
+    out64 (float64, before the final rounding), out_bits (uint16), and abs64 =
+    |D| + sum over outlier columns of |X[t, c] * W^[n, c]| + |bias[n]| (float64),
+    the magnitude that bounds the rounding error of any float32 evaluation of
+    O8-O11.
     """
     X = decode_bits(X_bits, dtype)
     idx = outlier_columns(X, threshold)
@@ -302,16 +299,21 @@ def linear_forward(X_bits, dtype, CB, SCB, bias_bits, threshold, rows=None, cols
     CA, SCA = absmax_quantize_rows(Xs, idx)
     acc = int8_accumulate(CA, CBs)
     D = dequantize(acc, SCA, SCBs)
+    abs64 = np.abs(D)
     if idx.size:
         What = recover_weight(CBs[:, idx], SCBs, dtype)
-        O = Xs[:, idx].astype(np.float64) @ What.T
+        Xo = Xs[:, idx].astype(np.float64)
+        O = Xo @ What.T
+        abs64 += np.abs(Xo) @ np.abs(What).T
     else:
         O = np.zeros_like(D)
     out64 = D + O
     if bias_bits is not None:
         b = decode_bits(bias_bits, dtype).astype(np.float64)
-        out64 = out64 + (b if cols is None else b[np.asarray(cols)])[None, :]
-    return dict(idx=idx, CA=CA, SCA=SCA, acc=acc, out64=out64,
+        b = (b if cols is None else b[np.asarray(cols)])[None, :]
+        out64 = out64 + b
+        abs64 += np.abs(b)
+    return dict(idx=idx, CA=CA, SCA=SCA, acc=acc, out64=out64, abs64=abs64,
                 out_bits=round_to_dtype_bits(out64, dtype))
 
 

@@ -6,20 +6,14 @@ import numpy as np
 import pytest
 
 import oracle as O
-from tests.gpu_helpers import OUT_TOL, bits_of, normwise_rel, to_dev
-from workloads import CONFIG_ORDER, config_case
+from tests.gpu_helpers import assert_out, bits_of, to_dev
+from tests import parity_cases as PC
+from workloads import config_case
 
 pytestmark = pytest.mark.gpu
 
 
-def _sample(n, k_edge, k_rand, seed):
-    rng = np.random.default_rng(seed)
-    edge = list(range(min(k_edge, n))) + list(range(max(0, n - k_edge), n))
-    mid = rng.choice(n, size=min(k_rand, n), replace=False).tolist()
-    return np.array(sorted(set(edge + mid)), dtype=np.int64)
-
-
-@pytest.mark.parametrize("name", [c for c in CONFIG_ORDER if c != "tiny"])
+@pytest.mark.parametrize("name", PC.FULL_CONFIGS)
 def test_config_parity(name):
     import torch
     import bit_quantized_matmul_amd as B
@@ -36,7 +30,7 @@ def test_config_parity(name):
     assert torch.equal(out, out_b)
 
     # weight codes on sampled rows
-    wrows = _sample(case.N, 64, 192, 1)
+    wrows = PC.sample_indices(case.N, 64, 192, 1)
     rCB, rSCB = O.quantize_weight_bits(case.W, case.dtype, rows=wrows)
     assert np.array_equal(CB[torch.from_numpy(wrows).cuda()].cpu().numpy(), rCB)
     assert np.array_equal(SCB[torch.from_numpy(wrows).cuda()].cpu().numpy(), rSCB)
@@ -53,8 +47,7 @@ def test_config_parity(name):
     del Xf, rCA
 
     # accumulators and outputs on a sampled block
-    rows = _sample(case.T, 8, 24, 2)
-    cols = _sample(case.N, 128, 768, 3)
+    rows, cols = PC.config_sample(case)
     sCB, sSCB = O.quantize_weight_bits(case.W, case.dtype, rows=cols)
     CBfull_cols = np.zeros((case.N, case.K), np.int8)  # only the sampled rows are read
     SCBfull = np.zeros(case.N, np.float32)
@@ -66,6 +59,6 @@ def test_config_parity(name):
     acc = ws.acc[ri][:, ci].cpu().numpy()
     assert np.array_equal(acc, r["acc"])
     ob = bits_of(out[ri][:, ci])
-    err = normwise_rel(ob, r["out64"], case.dtype)
-    print(f"[config parity] {name}: n_idx={n} out normwise rel err={err:.3e}", flush=True)
-    assert err <= OUT_TOL
+    err, ratio = assert_out(ob, r, case.dtype)
+    print(f"[config parity] {name}: n_idx={n} out normwise rel err={err:.3e}, "
+          f"worst element {ratio:.3f} x bound", flush=True)

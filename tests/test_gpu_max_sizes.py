@@ -6,12 +6,12 @@ import numpy as np
 import pytest
 
 import oracle as O
-from tests.gpu_helpers import OUT_TOL, bits_of, normwise_rel, to_dev
-from workloads import random_case
+from tests.gpu_helpers import assert_out, bits_of, to_dev
+from tests import parity_cases as PC
 
 pytestmark = pytest.mark.gpu
 
-KMAX = 133144
+KMAX = PC.KMAX
 
 
 def _lib():
@@ -43,16 +43,16 @@ def test_extreme_accumulator_at_max_k():
     CBr, SCBr = O.quantize_weight_bits(W.view(np.uint16), "f16")
     r = O.linear_forward(Xb, "f16", CBr, SCBr, None, 6.0)
     assert np.array_equal(acc, r["acc"])
-    assert normwise_rel(bits_of(out), r["out64"], "f16") <= OUT_TOL
+    assert_out(bits_of(out), r, "f16")
 
 
-@pytest.mark.parametrize("T,K,N", [(8, KMAX - 8, 24), (3, KMAX, 5), (40, KMAX, 33)])
+@pytest.mark.parametrize("T,K,N", PC.MAX_K_SHAPES)
 def test_random_at_max_k(T, K, N):
     """K % 16 == 0 at T <= 16: the non-fused decode kernel; K % 16 != 0: the
     small-tile kernel with its ragged K tail."""
     import torch
     B = _lib()
-    case = random_case(T, K, N, seed=K % 97 + T, n_out=3)
+    case = PC.max_k_case(T, K, N)
     X = to_dev(case.X, "f16")
     W = to_dev(case.W, "f16")
     bias = to_dev(case.bias, "f16")
@@ -66,7 +66,7 @@ def test_random_at_max_k(T, K, N):
     assert np.array_equal(ws.idx[:n].cpu().numpy(), r["idx"])
     assert np.array_equal(ws.CA.cpu().numpy(), r["CA"])
     assert np.array_equal(ws.acc.cpu().numpy(), r["acc"])
-    assert normwise_rel(bits_of(out), r["out64"], "f16") <= OUT_TOL
+    assert_out(bits_of(out), r, "f16")
 
 
 def test_large_tiles_at_large_k_sampled():
@@ -76,15 +76,14 @@ def test_large_tiles_at_large_k_sampled():
     import torch
     B = _lib()
     T, K, N = 520, 133120, 600
-    case = random_case(T, K, N, seed=5, n_out=4)
+    case = PC.large_k_tiles_case()
     X = to_dev(case.X, "f16")
     W = to_dev(case.W, "f16")
     CB, SCB = B.lli8_quant_weight_rowwise(W)
     del W
     out, ws = B.lli8_int8_linear(X, CB, SCB, None, case.threshold, want_acc=True)
     torch.cuda.synchronize()
-    rows = np.array([0, 1, 255, 256, 511, 512, 519])
-    cols = np.array([0, 7, 255, 256, 300, 511, 512, 599])
+    rows, cols = PC.LARGE_K_ROWS, PC.LARGE_K_COLS
     sCB, sSCB = O.quantize_weight_bits(case.W, "f16", rows=cols)
     assert np.array_equal(CB[torch.from_numpy(cols).cuda()].cpu().numpy(), sCB)
     CBs = np.zeros((N, K), np.int8)
@@ -96,4 +95,4 @@ def test_large_tiles_at_large_k_sampled():
     ri, ci = torch.from_numpy(rows).cuda(), torch.from_numpy(cols).cuda()
     assert np.array_equal(ws.CA[ri].cpu().numpy(), r["CA"])
     assert np.array_equal(ws.acc[ri][:, ci].cpu().numpy(), r["acc"])
-    assert normwise_rel(bits_of(out[ri][:, ci]), r["out64"], "f16") <= OUT_TOL
+    assert_out(bits_of(out[ri][:, ci]), r, "f16")

@@ -173,12 +173,15 @@ def config_case(name: str, seed: int = 0) -> Case:
 
 
 def random_case(T, K, N, dtype=F16, seed=0, n_out=3, bias="normal",
-                threshold=6.0, out_lo=6.0, out_hi=60.0) -> Case:
-    """A small case of arbitrary shape for parity sweeps."""
+                threshold=6.0, out_lo=6.0, out_hi=60.0, bias_sigma=0.5) -> Case:
+    """A small case of arbitrary shape for parity sweeps.  The bias is drawn
+    N(0, 0.5), the size of a typical output element (N(0, 1) activations
+    times N(0, 0.02) weights summed over a few hundred to a few thousand
+    features), so that a lost or misplaced bias term shows in every output."""
     n_out = min(n_out, K)
     return make_case(f"rand_{T}x{K}x{N}_{dtype}_{seed}", T, K, N, dtype,
                      n_out=n_out, out_lo=out_lo, out_hi=out_hi, bias=bias,
-                     threshold=threshold, seed=seed)
+                     bias_sigma=bias_sigma, threshold=threshold, seed=seed)
 
 
 def matrix_bits(R: int, C: int, dtype: str = F16, seed: int = 0) -> np.ndarray:
