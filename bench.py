@@ -7,6 +7,14 @@ column scan, row-wise activation quantisation, int8 GEMM with the fused
 dequantisation, 16-bit outlier product and bias (and, for the workloads whose
 weights are quantised on every call, the weight quantisation before it).
 
+The headline workload (default) is the 175B-class FFN up-projection, 4096
+tokens x 12288 -> 49152 in fp16, the largest configuration, on which the
+metric is quoted.  The same JSON line carries, under "workloads", the
+16-token decode step (4096 -> 4096, HBM-bound) and the 4096-token 7B-class
+MLP up-projection (4096 -> 11008), each measured the same way, so one run
+covers the int8-MFMA targets of the 4096-token shapes and the HBM target of
+the decode shape (--extra "" measures the headline only).
+
 Timing protocol.  All inputs are resident in HBM before the timed region.
 Untimed steps run for --settle-ms (200 ms) so the clocks have left idle, then
 the W warm-up steps.
@@ -38,8 +46,8 @@ if ROOT not in sys.path:
 
 METRIC = "LLM.int8 linear effective TOPS (2TNK/t) + % of MI355X int8-MFMA/HBM roofline"
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
-INT8_PEAK_TOPS = 5000.0        # MI355X dense int8 MFMA, TOP/s
-BF16_PEAK_TFLOPS = 2500.0      # MI355X dense fp16/bf16 MFMA, TFLOP/s
+INT8_PEAK_TOPS = 5033.2        # MI355X dense int8 MFMA: 256 CUs x 2.4 GHz x 8192 ops/clock, TOP/s
+BF16_PEAK_TFLOPS = 2516.6      # MI355X dense fp16/bf16 MFMA, TFLOP/s
 
 
 def parse():
@@ -47,7 +55,10 @@ def parse():
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=50)
     p.add_argument("--warmup", type=int, default=10)
-    p.add_argument("--workload", default="decode")
+    p.add_argument("--workload", default="ffn_175b")
+    p.add_argument("--extra", default="decode,prefill_mlp_up",
+                   help="comma-separated workloads measured after the headline one and reported "
+                        "under 'workloads' in the same line")
     p.add_argument("--rotate-mib", type=float, default=768.0,
                    help="input copies are rotated until one pass moves this many MiB")
     p.add_argument("--cpu-seconds", type=float, default=10.0, help="target CPU-oracle time")
@@ -87,6 +98,8 @@ def kernel_bytes(name, case, n_idx):
         return 4 * ((K + 31) // 32)
     if name == "recover_outliers":  # CB at the outlier columns in, recovered rows out
         return N * n_idx + 4 * N + 4 * n_idx + 2 * N * npad
+    if name == "recover_weight":  # CB and SCB in, the 16-bit weight out
+        return N * K + 4 * N + 2 * N * K
     return 0
 
 
@@ -102,7 +115,7 @@ KERNEL_SOURCES = {
     "int8_gemm": "lli8_gemm.hip", "decode_fused": "lli8_decode.hip", "quant_activations": "lli8_quant.hip",
     "outlier_scan": "lli8_quant.hip", "quant_weight": "lli8_quant.hip", "bitmap_clear": "lli8_quant.hip",
     "activation_split": "lli8_quant.hip",
-    "recover_outliers": "lli8_quant.hip",
+    "recover_outliers": "lli8_quant.hip", "recover_weight": "lli8_recover.hip",
 }
 
 
@@ -141,11 +154,12 @@ def cpu_baseline(case, CB_np, SCB_np, seconds):
     """The CPU oracle on the host, on a bounded sample of the same workload."""
     import numpy as np
     import oracle as O
-    try:
-        from threadpoolctl import threadpool_info
-        cores = max([d.get("num_threads", 1) for d in threadpool_info()] or [1])
+    cores = len(os.sched_getaffinity(0))
+    try:  # the BLAS pool the oracle's matrix products run on, sized to the cores it may use
+        from threadpoolctl import threadpool_limits
+        threadpool_limits(cores)
     except Exception:
-        cores = 1
+        pass
     # rows of X per oracle call: whole workload when small, else a row sample
     flops_per_row = 2.0 * case.N * case.K
     rows = case.T if case.T * flops_per_row <= 2e10 else max(1, int(2e10 // flops_per_row))
@@ -163,9 +177,20 @@ def cpu_baseline(case, CB_np, SCB_np, seconds):
     t = sum(times) / len(times)
     what = "full workload" if sel is None else f"first {rows} of {case.T} rows (outlier scan over all rows)"
     return {"value": round(2.0 * rows * case.N * case.K / t / 1e12, 6), "unit": "TOPS",
-            "cores": int(cores), "kind": "oracle",
+            "cores": int(cores), "cpu": cpu_model(), "kind": "oracle",
             "sample": f"{what}; {len(times)} calls, mean {t * 1e3:.1f} ms per call"
                       + ("; weight quantisation included" if case.weights_each_call else "")}
+
+
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
 
 
 def bench_vectorwise(args):
@@ -241,29 +266,14 @@ def bench_vectorwise(args):
     print(json.dumps(line), flush=True)
 
 
-def main():
-    args = parse()
-    if args.gpus != 1:
-        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
-              "(this path is not sharded across GPUs).", file=sys.stderr)
-        sys.exit(2)
-    if args.copy_mib > 0:
-        copy_calibration(args.copy_mib)
-        return
-    if args.vectorwise:
-        bench_vectorwise(args)
-        return
-
+def measure(name, case, args):
+    """One workload: inputs resident in rotated copies, the timed region, the
+    per-kernel trace pass; returns the JSON line without the CPU baseline."""
     import numpy as np
     import torch
     import bit_quantized_matmul_amd as B
-    from workloads import CONFIGS, config_case
 
-    if args.workload not in CONFIGS:
-        sys.exit(f"unknown workload {args.workload!r}; choose from {sorted(CONFIGS)}")
     dev = torch.device("cuda:0")
-    torch.cuda.set_device(dev)
-    case = config_case(args.workload)
 
     def to_dev(bits):
         t = torch.from_numpy(np.ascontiguousarray(bits).view(np.int16))
@@ -292,7 +302,11 @@ def main():
         copies.append(cp)
     if not case.weights_each_call:
         del W0
-    ws = B.Workspace(T, K, N, X0.dtype, dev)
+    # with most columns outliers (the stress workloads) the caller gives the
+    # scratch room for every recovered outlier weight; otherwise the default
+    # one-buffer workspace (room for 8 outlier chunks)
+    scratch = "full" if case.weights_each_call else None
+    ws = B.Workspace(T, K, N, X0.dtype, dev, scratch_bytes=scratch)
     out = torch.empty((T, N), dtype=X0.dtype, device=dev)
 
     def bound_step(i):
@@ -373,8 +387,8 @@ def main():
     kern_ms = {}
     for i in range(args.steps):
         bound_step(i)
-        for name, kms in B.lli8_trace_read():
-            kern_ms.setdefault(name, []).append(kms)
+        for kname, kms in B.lli8_trace_read():
+            kern_ms.setdefault(kname, []).append(kms)
     torch.cuda.synchronize()
     B.lli8_trace_enable(False)
     avg = {k: sum(v) / len(v) for k, v in kern_ms.items()}
@@ -395,7 +409,7 @@ def main():
         gbs = kernel_bytes(dom, case, n_idx) / (dom_ms * 1e-3) / 1e9
         roof = {"bound": "hbm", "achieved": round(gbs, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s"}
     roof["frac"] = round(roof["achieved"] / roof["peak"], 4)
-    roof["traffic"] = measured_traffic(args.workload, dom)
+    roof["traffic"] = measured_traffic(name, dom)
     roof["kernel"] = dom
     roof["kernel_ms"] = round(dom_ms, 5)
 
@@ -404,9 +418,10 @@ def main():
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 5),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "int8",
         "data": "synthetic",
-        "config": {"workload": args.workload, "api": args.api, "T": T, "K": K, "N": N, "act_dtype": case.dtype,
+        "config": {"workload": name, "api": args.api, "T": T, "K": K, "N": N, "act_dtype": case.dtype,
                    "threshold": case.threshold, "n_idx": n_idx, "bias": case.bias is not None,
                    "weights": "quantised every call" if case.weights_each_call else "pre-quantised",
+                   "scratch": "full" if scratch else "default",
                    "input_copies_rotated": R, "rotation_mib": round(R * copy_bytes / 2 ** 20, 1),
                    "settle_steps": n_settle,
                    "step_algorithmic_bytes": step_bytes(case),
@@ -415,6 +430,47 @@ def main():
                    "timed_wall_s": round(t_wall, 3)},
         "roofline": roof,
     }
+    return line
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
+              "(this path is not sharded across GPUs).", file=sys.stderr)
+        sys.exit(2)
+    if args.copy_mib > 0:
+        copy_calibration(args.copy_mib)
+        return
+    if args.vectorwise:
+        bench_vectorwise(args)
+        return
+
+    import torch
+    from workloads import CONFIGS, config_case
+
+    names = [args.workload] + [w for w in args.extra.split(",") if w and w != args.workload]
+    for w in names:
+        if w not in CONFIGS:
+            sys.exit(f"unknown workload {w!r}; choose from {sorted(CONFIGS)}")
+    torch.cuda.set_device(torch.device("cuda:0"))
+    case = config_case(args.workload)
+    line = measure(args.workload, case, args)
+    print(f"[bench] {args.workload}: {line['ms_per_step']} ms per step, {line['value']} TOPS", file=sys.stderr,
+          flush=True)
+    extra = {}
+    for w in names[1:]:
+        torch.cuda.empty_cache()
+        sub = measure(w, config_case(w), args)
+        print(f"[bench] {w}: {sub['ms_per_step']} ms per step, {sub['value']} TOPS", file=sys.stderr, flush=True)
+        c = sub["config"]
+        extra[w] = {"value": sub["value"], "unit": sub["unit"], "ms_per_step": sub["ms_per_step"],
+                    "T": c["T"], "K": c["K"], "N": c["N"], "n_idx": c["n_idx"],
+                    "step_hbm_frac": c["step_hbm_frac"], "kernels_ms": c["kernels_ms"],
+                    "roofline": sub["roofline"]}
+    if extra:
+        line["workloads"] = extra
+    torch.cuda.empty_cache()
     if not args.no_cpu_baseline:
         import oracle as O
         CB_np, SCB_np = O.quantize_weight_bits(case.W, case.dtype)  # the oracle's own codes

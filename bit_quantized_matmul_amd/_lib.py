@@ -77,6 +77,12 @@ def lib() -> ctypes.CDLL:
     L.lli8_int8_linear.restype = i32
     L.lli8_quant_vectorwise.argtypes = [vp, i64, i64, i32, i32, i32, vp, vp, vp, vp]
     L.lli8_quant_vectorwise.restype = i32
+    L.lli8_recover_weight.argtypes = [vp, vp, i64, i64, i32, vp, vp]
+    L.lli8_recover_weight.restype = i32
+    L.lli8_workspace_bytes.argtypes = [i64, i64, i64, i32]
+    L.lli8_workspace_bytes.restype = ctypes.c_size_t
+    L.lli8_workspace_carve.argtypes = [vp, ctypes.c_size_t, i64, i64, i64, i32, ctypes.POINTER(_Workspace)]
+    L.lli8_workspace_carve.restype = i32
     L.lli8_scratch_bytes.argtypes = [i64, i64, i32]
     L.lli8_scratch_bytes.restype = ctypes.c_size_t
     L.lli8_scratch_bytes_full.argtypes = [i64, i64, i64, i32]
@@ -140,6 +146,32 @@ def _ptr(t) -> Optional[int]:
     return t.data_ptr()
 
 
+def _gpu(t, name: str):
+    """t must be a contiguous tensor on a GPU; returns its device."""
+    if not t.is_cuda:
+        raise ValueError(f"{name} is on {t.device}: lli8 runs on the GPU only (no CPU path)")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    return t.device
+
+
+def _arg(t, name: str, device, dtype, numel: int, shape=None):
+    """A caller buffer: on `device`, of `dtype`, contiguous, holding `numel`
+    elements (and of `shape` when given).  Raises before anything is enqueued:
+    a host tensor or a short buffer would make a kernel read or write outside
+    device memory."""
+    if t.device != device:
+        raise ValueError(f"{name} is on {t.device}, the other operands on {device}")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} has dtype {t.dtype}, expected {dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+    if t.numel() != numel:
+        raise ValueError(f"{name} has {t.numel()} elements, expected {numel}")
+
+
 _raw_stream = None
 
 
@@ -162,11 +194,16 @@ def _stream(device, stream=None) -> int:
 def lli8_quant_weight_rowwise(W, CB=None, SCB=None, stream=None):
     """W [N, K] fp16/bf16 on the GPU -> (CB int8 [N, K], SCB fp32 [N])."""
     torch = _torch()
+    if W.dim() != 2:
+        raise ValueError("W must be 2-D [N, K]")
+    dev = _gpu(W, "W")
     N, K = W.shape
     if CB is None:
-        CB = torch.empty((N, K), dtype=torch.int8, device=W.device)
+        CB = torch.empty((N, K), dtype=torch.int8, device=dev)
     if SCB is None:
-        SCB = torch.empty((N,), dtype=torch.float32, device=W.device)
+        SCB = torch.empty((N,), dtype=torch.float32, device=dev)
+    _arg(CB, "CB", dev, torch.int8, N * K, (N, K))
+    _arg(SCB, "SCB", dev, torch.float32, N)
     _check(lib().lli8_quant_weight_rowwise(_ptr(W), N, K, _dt(W), _ptr(CB), _ptr(SCB),
                                            _stream(W.device, stream)))
     return CB, SCB
@@ -176,18 +213,45 @@ def lli8_quant_rowwise_outliers(X, threshold: float, CA=None, SCA=None, bitmap=N
                                 n_idx=None, stream=None):
     """X [T, K] -> (CA, SCA, bitmap, idx, n_idx); idx[:n_idx] are the outlier columns."""
     torch = _torch()
+    dev = _gpu(X, "X")
     X2 = X.reshape(-1, X.shape[-1])
     T, K = X2.shape
-    dev = X.device
     CA = torch.empty((T, K), dtype=torch.int8, device=dev) if CA is None else CA
     SCA = torch.empty((T,), dtype=torch.float32, device=dev) if SCA is None else SCA
     bitmap = torch.empty(((K + 31) // 32,), dtype=torch.int32, device=dev) if bitmap is None else bitmap
     idx = torch.empty((K,), dtype=torch.int32, device=dev) if idx is None else idx
     n_idx = torch.empty((1,), dtype=torch.int32, device=dev) if n_idx is None else n_idx
+    _arg(CA, "CA", dev, torch.int8, T * K)
+    _arg(SCA, "SCA", dev, torch.float32, T)
+    _arg(bitmap, "bitmap", dev, torch.int32, (K + 31) // 32)
+    _arg(idx, "idx", dev, torch.int32, K)
+    _arg(n_idx, "n_idx", dev, torch.int32, 1)
     _check(lib().lli8_quant_rowwise_outliers(_ptr(X2), T, K, _dt(X2), float(threshold), _ptr(CA),
                                              _ptr(SCA), _ptr(bitmap), _ptr(idx), _ptr(n_idx),
                                              _stream(dev, stream)))
     return CA, SCA, bitmap, idx, n_idx
+
+
+def lli8_recover_weight(CB, SCB, dtype=None, W=None, stream=None):
+    """(CB * SCB) / 127 in a 16-bit dtype (float16 by default), the weight the
+    int8 codes stand for: W[n, k] = dtype(fl32(fl32(CB[n, k] * SCB[n]) / 127))."""
+    torch = _torch()
+    if CB.dim() != 2:
+        raise ValueError("CB must be 2-D [N, K]")
+    dev = _gpu(CB, "CB")
+    N, K = CB.shape
+    _arg(CB, "CB", dev, torch.int8, N * K)
+    _arg(SCB, "SCB", dev, torch.float32, N)
+    dtype = (W.dtype if W is not None else torch.float16) if dtype is None else dtype
+    if W is None:
+        W = torch.empty((N, K), dtype=dtype, device=dev)
+    _arg(W, "W", dev, dtype, N * K)
+    _check(lib().lli8_recover_weight(_ptr(CB), _ptr(SCB), N, K, _dt(W), _ptr(W), _stream(dev, stream)))
+    return W
+
+
+def lli8_workspace_bytes(T: int, K: int, N: int, dtype: int = LLI8_F16) -> int:
+    return int(lib().lli8_workspace_bytes(T, K, N, dtype))
 
 
 def lli8_quant_vectorwise(X, scheme: str = "absmax", axis: str = "rows", codes=None, scale=None,
@@ -203,12 +267,15 @@ def lli8_quant_vectorwise(X, scheme: str = "absmax", axis: str = "rows", codes=N
         raise ValueError("X must be 2-D [R, C]")
     R, C = X.shape
     nvec = R if axis == "rows" else C
-    dev = X.device
+    dev = _gpu(X, "X")
     codes = torch.empty((R, C), dtype=torch.int8, device=dev) if codes is None else codes
     scale = torch.empty((nvec,), dtype=torch.float32, device=dev) if scale is None else scale
+    _arg(codes, "codes", dev, torch.int8, R * C)
+    _arg(scale, "scale", dev, torch.float32, nvec)
     zp = None
     if scheme == "zeropoint":
         zp = torch.empty((nvec,), dtype=torch.int32, device=dev) if zero_point is None else zero_point
+        _arg(zp, "zero_point", dev, torch.int32, nvec)
     _check(lib().lli8_quant_vectorwise(_ptr(X), R, C, _dt(X),
                                        LLI8_ZEROPOINT if scheme == "zeropoint" else LLI8_ABSMAX,
                                        LLI8_ROWS if axis == "rows" else LLI8_COLS,
@@ -217,23 +284,54 @@ def lli8_quant_vectorwise(X, scheme: str = "absmax", axis: str = "rows", codes=N
 
 
 class Workspace:
-    """Caller-owned buffers of one forward call (torch tensors on one device)."""
+    """Caller-owned buffers of one forward call (torch tensors on one device).
+
+    By default one device buffer of lli8_workspace_bytes(T, K, N) bytes,
+    split by lli8_workspace_carve: CA, SCA, bitmap, idx, n_idx and a scratch
+    with room for the recovered weights of 8 outlier chunks (256 columns).
+    scratch_bytes="full" gives room for every possible outlier column
+    (lli8_scratch_bytes_full: N * K * 2 bytes more, the fast path when most
+    columns are outliers); an integer gives exactly that much scratch (at
+    least lli8_scratch_bytes)."""
 
     def __init__(self, T: int, K: int, N: int, dtype, device, want_acc: bool = False,
-                 scratch_bytes: Optional[int] = None):
-        """scratch_bytes: None gives room for the recovered weights of every
-        possible outlier column (lli8_scratch_bytes_full); a smaller size is used
-        as far as it goes (at least lli8_scratch_bytes)."""
+                 scratch_bytes=None):
         torch = _torch()
         self.T, self.K, self.N = T, K, N
-        self.CA = torch.empty((T, K), dtype=torch.int8, device=device)
-        self.SCA = torch.empty((max(T, 1),), dtype=torch.float32, device=device)
-        self.bitmap = torch.empty(((K + 31) // 32,), dtype=torch.int32, device=device)
-        self.idx = torch.empty((K,), dtype=torch.int32, device=device)
-        self.n_idx = torch.zeros((1,), dtype=torch.int32, device=device)
+        self.device = torch.device(device)
+        if self.device.type == "cuda" and self.device.index is None:
+            self.device = torch.device("cuda", torch.cuda.current_device())
         self.acc = torch.empty((T, N), dtype=torch.int32, device=device) if want_acc else None
-        nbytes = lli8_scratch_bytes_full(T, K, N, LLI8_F16) if scratch_bytes is None else int(scratch_bytes)
-        self.scratch = torch.empty((max(nbytes, 16),), dtype=torch.uint8, device=device)
+        if scratch_bytes is None:
+            nbytes = int(lib().lli8_workspace_bytes(T, K, N, LLI8_F16))
+            if nbytes == 0:
+                raise ValueError(f"invalid workspace sizes T={T} K={K} N={N}")
+            self.buffer = torch.empty((nbytes,), dtype=torch.uint8, device=device)
+            st = _Workspace()
+            _check(lib().lli8_workspace_carve(self.buffer.data_ptr(), nbytes, T, K, N, LLI8_F16,
+                                              ctypes.byref(st)))
+            base = self.buffer.data_ptr()
+
+            def view(ptr, count, dtype, shape):
+                o = ptr - base
+                return self.buffer[o:o + count * dtype.itemsize].view(dtype).view(shape)
+            self.CA = view(st.CA, T * K, torch.int8, (T, K))
+            self.SCA = view(st.SCA, max(T, 1), torch.float32, (max(T, 1),))
+            self.bitmap = view(st.bitmap, (K + 31) // 32, torch.int32, ((K + 31) // 32,))
+            self.idx = view(st.idx, K, torch.int32, (K,))
+            self.n_idx = view(st.n_idx, 1, torch.int32, (1,))
+            self.n_idx.zero_()
+            self.scratch = view(st.scratch, max(st.scratch_bytes, 16), torch.uint8, (max(st.scratch_bytes, 16),))
+            nbytes = st.scratch_bytes
+        else:
+            self.CA = torch.empty((T, K), dtype=torch.int8, device=device)
+            self.SCA = torch.empty((max(T, 1),), dtype=torch.float32, device=device)
+            self.bitmap = torch.empty(((K + 31) // 32,), dtype=torch.int32, device=device)
+            self.idx = torch.empty((K,), dtype=torch.int32, device=device)
+            self.n_idx = torch.zeros((1,), dtype=torch.int32, device=device)
+            nbytes = (lli8_scratch_bytes_full(T, K, N, LLI8_F16) if scratch_bytes == "full"
+                      else int(scratch_bytes))
+            self.scratch = torch.empty((max(nbytes, 16),), dtype=torch.uint8, device=device)
         self._struct = _Workspace(self.CA.data_ptr(), self.SCA.data_ptr(), self.bitmap.data_ptr(),
                                   self.idx.data_ptr(), self.n_idx.data_ptr(),
                                   self.acc.data_ptr() if self.acc is not None else None,
@@ -256,15 +354,25 @@ def lli8_int8_linear(X, CB, SCB, bias=None, threshold: float = 6.0, out=None,
     want_acc) of this call.
     """
     torch = _torch()
+    dev = _gpu(X, "X")
     X2 = X if X.dim() == 2 else X.reshape(-1, X.shape[-1])
     T, K = X2.shape
+    if CB.dim() != 2 or CB.shape[1] != K:
+        raise ValueError(f"CB has shape {tuple(CB.shape)}, X has K={K}")
     N = CB.shape[0]
-    if CB.shape[1] != K:
-        raise ValueError(f"CB has K={CB.shape[1]}, X has K={K}")
-    if ws is None or not ws.fits(T, K, N, want_acc):
-        ws = Workspace(T, K, N, X.dtype, X.device, want_acc)
+    _arg(CB, "CB", dev, torch.int8, N * K)
+    _arg(SCB, "SCB", dev, torch.float32, N)
+    if bias is not None:
+        _arg(bias, "bias", dev, X.dtype, N)
+    if ws is None:
+        ws = Workspace(T, K, N, X.dtype, dev, want_acc)
+    elif not ws.fits(T, K, N, want_acc) or ws.device != dev:
+        raise ValueError(f"workspace for T={ws.T} K={ws.K} N={ws.N} on {ws.device}"
+                         f"{' without acc' if ws.acc is None else ''} does not fit T={T} K={K} N={N} on {dev}")
     if out is None:
-        out = torch.empty((T, N), dtype=X.dtype, device=X.device)
+        out = torch.empty((T, N), dtype=X.dtype, device=dev)
+    else:
+        _arg(out, "out", dev, X.dtype, T * N)
     _check(lib().lli8_int8_linear(_ptr(X2), T, K, N, _dt(X2), _ptr(CB), _ptr(SCB), _ptr(bias),
                                   float(threshold), _ptr(out), ctypes.byref(ws._struct),
                                   _stream(X.device, stream)))

@@ -1,6 +1,7 @@
 // C-ABI of the lli8 library: argument validation, then kernel launches on the
 // caller's stream.  Every argument is checked before anything is enqueued, so
 // a rejected call writes nothing.  No exception crosses the interface.
+#include <algorithm>
 #include <math.h>
 #include <stdarg.h>
 #include <stdio.h>
@@ -141,13 +142,49 @@ lli8_status_t enqueue_activation_split(const void* X, int64_t T, int64_t K, int 
 // weights [chunks][N][32] (16-bit each).
 size_t xo_bytes(int64_t T, int64_t K) { return (size_t)(T * ((K + 31) / 32 * 32) * 2); }
 
+// One-buffer workspace (lli8_workspace_bytes / lli8_workspace_carve): the
+// pieces in this order, each starting on a 256-byte boundary.
+size_t up256(size_t b) { return (b + 255) & ~(size_t)255; }
+
+struct Carve {
+  size_t ca, sca, bitmap, idx, n_idx, scratch, scratch_bytes, total;
+};
+
+Carve carve_layout(int64_t T, int64_t K, int64_t N) {
+  Carve c;
+  size_t o = 0;
+  c.ca = o;
+  o += up256((size_t)(T * K));
+  c.sca = o;
+  o += up256((size_t)(T > 0 ? T : 1) * 4);
+  c.bitmap = o;
+  o += up256((size_t)((K + 31) / 32) * 4);
+  c.idx = o;
+  o += up256((size_t)K * 4);
+  c.n_idx = o;
+  o += 256;
+  c.scratch = o;
+  const int64_t chunks = std::min<int64_t>((K + 31) / 32, LLI8_WORKSPACE_WO_CHUNKS);
+  c.scratch_bytes = (T > 0 ? xo_bytes(T, K) : 0) + (size_t)(N * 64 * chunks);
+  o += up256(c.scratch_bytes);
+  c.total = o;
+  return c;
+}
+
 }  // namespace
 
 extern "C" {
 
 const char* lli8_version(void) { return "0.1.0"; }
 
-void lli8_trace_enable(int on) { g_trace.on = on != 0; }
+void lli8_trace_enable(int on) {
+  g_trace.on = on != 0;
+  if (!g_trace.on && g_trace.created) {  // release the events now, not at process exit
+    for (int i = 0; i < 2 * LLI8_TRACE_MAX; ++i) (void)hipEventDestroy(g_trace.ev[i]);
+    g_trace.created = false;
+    g_trace.n = 0;
+  }
+}
 
 lli8_status_t lli8_trace_read(lli8_trace_t* out) {
   if (out == nullptr) return fail(LLI8_ERR_NULL, "trace output is NULL");
@@ -190,6 +227,46 @@ size_t lli8_scratch_bytes(int64_t T, int64_t K, lli8_dtype_t dtype) {
 size_t lli8_scratch_bytes_full(int64_t T, int64_t K, int64_t N, lli8_dtype_t dtype) {
   if (T <= 0 || K <= 0 || N <= 0) return lli8_scratch_bytes(T, K, dtype);
   return xo_bytes(T, K) + (size_t)(N * ((K + 31) / 32 * 32) * 2);
+}
+
+size_t lli8_workspace_bytes(int64_t T, int64_t K, int64_t N, lli8_dtype_t dtype) {
+  (void)dtype;  // both dtypes are 16-bit
+  if (T < 0 || K < 1 || N < 1) return 0;
+  return carve_layout(T, K, N).total;
+}
+
+lli8_status_t lli8_workspace_carve(void* base, size_t bytes, int64_t T, int64_t K, int64_t N, lli8_dtype_t dtype,
+                                   lli8_workspace_t* ws) {
+  TRY(check_dtype(dtype));
+  TRY(check_sizes(T, K, N));
+  if (ws == nullptr) return fail(LLI8_ERR_NULL, "workspace struct is NULL");
+  REQUIRE(base, "base");
+  const Carve c = carve_layout(T, K, N);
+  if (bytes < c.total) return fail(LLI8_ERR_WORKSPACE, "workspace needs %zu bytes, got %zu", c.total, bytes);
+  char* b = static_cast<char*>(base);
+  ws->CA = reinterpret_cast<int8_t*>(b + c.ca);
+  ws->SCA = reinterpret_cast<float*>(b + c.sca);
+  ws->bitmap = reinterpret_cast<uint32_t*>(b + c.bitmap);
+  ws->idx = reinterpret_cast<int32_t*>(b + c.idx);
+  ws->n_idx = reinterpret_cast<int32_t*>(b + c.n_idx);
+  ws->acc = nullptr;
+  ws->scratch = b + c.scratch;
+  ws->scratch_bytes = c.scratch_bytes;
+  return LLI8_OK;
+}
+
+lli8_status_t lli8_recover_weight(const int8_t* CB, const float* SCB, int64_t N, int64_t K, lli8_dtype_t dtype,
+                                  void* W, void* stream) {
+  TRY(check_dtype(dtype));
+  if (N < 0 || K < 0) return fail(LLI8_ERR_SHAPE, "bad sizes N=%lld K=%lld", (long long)N, (long long)K);
+  if (N == 0 || K == 0) return LLI8_OK;
+  if (N * K > ((int64_t)1 << 40)) return fail(LLI8_ERR_UNSUPPORTED, "N*K too large");
+  REQUIRE(CB, "CB");
+  REQUIRE(SCB, "SCB");
+  REQUIRE(W, "W");
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  TRACED(s, "recover_weight", lli8::launch_recover_weight((int)dtype, CB, SCB, N, K, W, s));
+  return LLI8_OK;
 }
 
 lli8_status_t lli8_quant_weight_rowwise(const void* W, int64_t N, int64_t K, lli8_dtype_t dtype, int8_t* CB,

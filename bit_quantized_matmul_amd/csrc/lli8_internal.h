@@ -45,6 +45,10 @@ inline bool stream_gemm_route(int64_t T, int64_t N, int64_t K) {
   return (K % 16) == 0 && N <= 4096 && (T <= 32 || (T <= 64 && K <= 4096));
 }
 
+// W = dtype(fl32(fl32(CB * SCB) / 127)) for a whole [N, K] weight.
+hipError_t launch_recover_weight(int dt, const int8_t* CB, const float* SCB, int64_t N, int64_t K, void* W,
+                                 hipStream_t s);
+
 hipError_t launch_quant_vectorwise(int dt, const void* X, int64_t R, int64_t C, int zeropoint, int axis,
                                    int8_t* codes, float* scale, int32_t* zp, hipStream_t s);
 hipError_t launch_recover_outliers(int dt, const int8_t* CB, const float* SCB, int64_t N, int64_t K,

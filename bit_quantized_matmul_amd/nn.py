@@ -35,14 +35,9 @@ from typing import Optional
 
 import torch
 
-from ._lib import Workspace, lli8_int8_linear, lli8_quant_weight_rowwise, lli8_scratch_bytes, LLI8_F16
+from ._lib import Workspace, lli8_int8_linear, lli8_quant_weight_rowwise, lli8_recover_weight
 
 __all__ = ["Linear8bitLt", "Int8State", "save_int8", "load_int8"]
-
-# Room for the recovered weights of this many 32-column outlier chunks in each
-# forward's scratch (beyond it, the GEMM gathers the rest from CB itself).
-_WO_CHUNKS = 8
-
 
 class Int8State:
     """What the last forward left: its workspace (CA, SCA, the outlier set)."""
@@ -188,12 +183,12 @@ class Linear8bitLt(torch.nn.Module):
 
     def recovered_weight(self) -> torch.Tensor:
         """(CB * SCB) / 127 in the bias' 16-bit dtype (float16 without a bias):
-        the recovery form of "Integration into transformers".  A convenience
-        outside the forward path."""
+        the recovery form of "Integration into transformers", computed by the
+        library (lli8_recover_weight).  A convenience outside the forward path."""
         if not self.is_quantized:
             raise RuntimeError("the module is not quantised (has_fp16_weights=True or not on the GPU)")
         dt = self.bias.dtype if self.bias is not None else torch.float16
-        return ((self.weight.data.float() * self._scb[:, None]) / 127.0).to(dt)
+        return lli8_recover_weight(self.weight.data, self._scb, dtype=dt)
 
     # ----------------------------------------------------------- forward ----
 
@@ -201,10 +196,9 @@ class Linear8bitLt(torch.nn.Module):
         ws = self.state.ws
         if ws is not None and ws.fits(T, self.in_features, self.out_features, False) and ws.CA.device == device:
             return ws
-        K, N = self.in_features, self.out_features
-        chunks = min((K + 31) // 32, _WO_CHUNKS)
-        nbytes = lli8_scratch_bytes(T, K, LLI8_F16) + N * 64 * chunks
-        return Workspace(T, K, N, None, device, want_acc=False, scratch_bytes=nbytes)
+        # one buffer, with room for the recovered weights of 8 outlier chunks
+        # (256 columns); the GEMM gathers any further ones from CB itself
+        return Workspace(T, self.in_features, self.out_features, None, device, want_acc=False)
 
     def forward(self, x: torch.Tensor) -> torch.Tensor:
         if not x.is_cuda:

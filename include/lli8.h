@@ -23,8 +23,14 @@
  *   - Every tensor pointer is a DEVICE pointer to a caller-owned, contiguous,
  *     row-major buffer.  The library allocates no device memory and keeps no
  *     per-call state; all work is enqueued asynchronously on `stream`
- *     (a hipStream_t; NULL means the default stream).  No call synchronises
- *     the host.
+ *     (a hipStream_t passed as void*, so that this header needs no HIP
+ *     header; NULL means the default stream).  No call synchronises the
+ *     host.  Process-wide, the library remembers only each device's compute
+ *     unit count (looked up once, to size persistent grids) and the optional
+ *     kernel-timing events of lli8_trace_enable.
+ *   - Inputs are finite.  A NaN or infinite activation is outside the
+ *     contract: its column may or may not be flagged (the kernels compare
+ *     magnitude bit patterns, under which NaN exceeds every threshold).
  *   - X, W, bias and out share one 16-bit dtype (fp16 or bf16).  Codes (CA,
  *     CB) are int8 in [-127, 127]; scales (SCA, SCB) are fp32 and hold the
  *     row absmax itself; the dequantisation factor is SCA * SCB / 127^2.
@@ -120,6 +126,23 @@ typedef struct lli8_workspace {
   size_t scratch_bytes;
 } lli8_workspace_t;
 
+/* Bytes of one caller buffer that lli8_workspace_carve splits into all the
+ * buffers of a forward call for these sizes: CA, SCA, bitmap, idx, n_idx and
+ * a scratch with room for the recovered weights of LLI8_WORKSPACE_WO_CHUNKS
+ * 32-column outlier chunks (outlier columns beyond them are gathered from CB
+ * inside the GEMM tiles), each piece on a 256-byte boundary.  acc is not
+ * included.  0 for invalid sizes. */
+#define LLI8_WORKSPACE_WO_CHUNKS 8
+size_t lli8_workspace_bytes(int64_t T, int64_t K, int64_t N, lli8_dtype_t dtype);
+
+/* Fills *ws with pointers into the caller's device buffer `base` of `bytes`
+ * bytes (at least lli8_workspace_bytes(T, K, N, dtype)), acc = NULL.  Writes
+ * nothing to device memory.  Errors: LLI8_ERR_NULL (ws or base NULL),
+ * _ALIGN (base not 16-byte aligned), _SHAPE, _DTYPE, _UNSUPPORTED as for
+ * lli8_int8_linear, LLI8_ERR_WORKSPACE (buffer too small). */
+lli8_status_t lli8_workspace_carve(void* base, size_t bytes, int64_t T, int64_t K, int64_t N,
+                                   lli8_dtype_t dtype, lli8_workspace_t* ws);
+
 /* Bytes of scratch lli8_int8_linear needs for these sizes (the minimum:
  * the gathered outlier columns of X). */
 size_t lli8_scratch_bytes(int64_t T, int64_t K, lli8_dtype_t dtype);
@@ -148,6 +171,20 @@ lli8_status_t lli8_int8_linear(const void* X, int64_t T, int64_t K, int64_t N,
                                const float* SCB, const void* bias,
                                float threshold, void* out,
                                const lli8_workspace_t* ws, void* stream);
+
+/*
+ * Weight recovery, "Hugging Face integrates LLM.int8() ...", section
+ * "Integration into transformers": the weight the int8 codes stand for is
+ * (CB * SCB) / 127.  Evaluated left to right in fp32 and rounded once to the
+ * dtype, the values the forward's 16-bit outlier product uses:
+ *   W[n, k] = dtype(fl32(fl32(CB[n, k] * SCB[n]) / 127))
+ *   CB [N, K] int8, SCB [N] fp32 (read); W [N, K] fp16/bf16 (written).
+ * Not a step of lli8_int8_linear.  Errors: LLI8_ERR_NULL, _ALIGN, _SHAPE
+ * (N or K negative), _DTYPE, before anything is enqueued; N == 0 or K == 0 is
+ * a no-op.
+ */
+lli8_status_t lli8_recover_weight(const int8_t* CB, const float* SCB, int64_t N, int64_t K,
+                                  lli8_dtype_t dtype, void* W, void* stream);
 
 /*
  * Vector-wise quantisation of a 16-bit matrix on its own ("Hugging Face
@@ -186,7 +223,9 @@ lli8_status_t lli8_quant_vectorwise(const void* X, int64_t R, int64_t C, lli8_dt
  * ones are not recorded), one entry each with its name and elapsed
  * milliseconds, then starts a new record.  Not for concurrent use from
  * several threads.  Disabled by default; the events are created on first use
- * and kept until the process ends.
+ * while enabled, and lli8_trace_enable(0) destroys them (call it once the
+ * timed work has been read, so that no event outlives the caller's use of
+ * the HIP runtime).
  */
 #define LLI8_TRACE_MAX 8
 typedef struct lli8_trace {

@@ -26,7 +26,8 @@ def declared_functions():
 
 def test_header_declares_the_three_entry_points():
     names = declared_functions()
-    for n in ("lli8_quant_weight_rowwise", "lli8_quant_rowwise_outliers", "lli8_int8_linear"):
+    for n in ("lli8_quant_weight_rowwise", "lli8_quant_rowwise_outliers", "lli8_int8_linear",
+              "lli8_recover_weight", "lli8_workspace_bytes", "lli8_workspace_carve"):
         assert n in names
 
 
@@ -142,6 +143,84 @@ def test_validation_linear():
     assert call(ws=_ws(Lm, scratch_bytes=10)) == 8
     assert f(FAKE, 4, 8, 3, 0, FAKE, FAKE, None, 6.0, FAKE, None, None) == 1  # workspace NULL
     assert b"scratch" in L.lli8_last_error() or b"workspace" in L.lli8_last_error()
+
+
+def test_validation_recover_weight():
+    L = _lib().lib()
+    f = L.lli8_recover_weight
+    assert f(FAKE, FAKE, 4, 8, 3, FAKE, None) == 3                # dtype
+    assert f(FAKE, FAKE, -1, 8, 0, FAKE, None) == 2               # N < 0
+    assert f(FAKE, FAKE, 4, -8, 0, FAKE, None) == 2               # K < 0
+    for pos in (0, 1, 5):
+        args = [FAKE, FAKE, 4, 8, 0, FAKE, None]
+        args[pos] = None
+        assert f(*args) == 1
+        args[pos] = FAKE + 4
+        assert f(*args) == 4
+    assert f(None, None, 0, 8, 0, None, None) == 0                # nothing to do
+
+
+def test_workspace_bytes_and_carve():
+    """One buffer split into the forward's buffers: every piece 256-byte
+    aligned, in bounds, not overlapping, with room for 8 recovered-weight
+    chunks in the scratch; nothing is written to the (fake) device address."""
+    Lm = _lib()
+    L = Lm.lib()
+    for T, K, N in [(0, 64, 8), (1, 1, 1), (16, 4096, 4096), (4096, 12288, 49152), (37, 100, 3)]:
+        nb = Lm.lli8_workspace_bytes(T, K, N)
+        ws = Lm._Workspace()
+        base = 0x10000000
+        assert L.lli8_workspace_carve(base, nb, T, K, N, 0, ctypes.byref(ws)) == 0
+        pieces = [(ws.CA, T * K), (ws.SCA, 4 * max(T, 1)), (ws.bitmap, 4 * ((K + 31) // 32)),
+                  (ws.idx, 4 * K), (ws.n_idx, 4), (ws.scratch, ws.scratch_bytes)]
+        ends = []
+        for ptr, size in pieces:
+            ptr = ptr or base  # ctypes gives None for address 0 offsets; base is never 0 here
+            assert (ptr - base) % 256 == 0 and base <= ptr and ptr + size <= base + nb
+            ends.append((ptr, ptr + size))
+        ends.sort()
+        assert all(a[1] <= b[0] for a, b in zip(ends, ends[1:]))
+        assert ws.acc is None
+        assert ws.scratch_bytes >= Lm.lli8_scratch_bytes(T, K) + N * 64 * min((K + 31) // 32, 8)
+        assert L.lli8_workspace_carve(base, nb - 1, T, K, N, 0, ctypes.byref(ws)) == 8
+    assert L.lli8_workspace_carve(0x10000008, 1 << 30, 4, 8, 3, 0, ctypes.byref(ws)) == 4
+    assert L.lli8_workspace_carve(None, 1 << 30, 4, 8, 3, 0, ctypes.byref(ws)) == 1
+    assert L.lli8_workspace_carve(0x10000000, 1 << 30, 4, 8, 3, 0, None) == 1
+    assert L.lli8_workspace_carve(0x10000000, 1 << 30, 4, 0, 3, 0, ctypes.byref(ws)) == 2
+    assert Lm.lli8_workspace_bytes(4, 0, 3) == 0
+
+
+def test_binding_rejects_host_and_mismatched_tensors():
+    """The binding raises before any launch for tensors a kernel would read
+    or write out of bounds: host tensors, wrong dtypes, short buffers, a
+    workspace of other sizes (no GPU is touched: every check fails first)."""
+    import torch
+    Lm = _lib()
+    X = torch.zeros((4, 8), dtype=torch.float16)
+    with pytest.raises(ValueError, match="GPU only"):
+        Lm.lli8_int8_linear(X, torch.zeros((3, 8), dtype=torch.int8), torch.zeros(3))
+    with pytest.raises(ValueError, match="GPU only"):
+        Lm.lli8_quant_weight_rowwise(torch.zeros((3, 8), dtype=torch.float16))
+    with pytest.raises(ValueError, match="GPU only"):
+        Lm.lli8_quant_rowwise_outliers(X, 6.0)
+    with pytest.raises(ValueError, match="GPU only"):
+        Lm.lli8_quant_vectorwise(X)
+    with pytest.raises(ValueError, match="GPU only"):
+        Lm.lli8_recover_weight(torch.zeros((3, 8), dtype=torch.int8), torch.zeros(3))
+    # the per-operand checks, on tensors standing in for device tensors
+    dev = torch.device("cpu")
+    good = torch.zeros(6, dtype=torch.float32)
+    Lm._arg(good, "SCB", dev, torch.float32, 6)
+    with pytest.raises(TypeError, match="dtype"):
+        Lm._arg(good, "SCB", dev, torch.float16, 6)
+    with pytest.raises(ValueError, match="elements"):
+        Lm._arg(good, "SCB", dev, torch.float32, 7)
+    with pytest.raises(ValueError, match="shape"):
+        Lm._arg(good.view(2, 3), "CB", dev, torch.float32, 6, (3, 2))
+    with pytest.raises(ValueError, match="contiguous"):
+        Lm._arg(torch.zeros((3, 2)).t(), "CB", dev, torch.float32, 6)
+    with pytest.raises(ValueError, match="on meta"):
+        Lm._arg(torch.zeros(6, device="meta"), "bias", dev, torch.float32, 6)
 
 
 def test_product_path_has_no_cpu_fallback():

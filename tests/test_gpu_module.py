@@ -9,7 +9,8 @@ import numpy as np
 import pytest
 
 import oracle as O
-from tests.gpu_helpers import OUT_TOL, bits_of, normwise_rel, to_dev
+from tests.gpu_helpers import assert_out, bits_of, to_dev
+from tests import parity_cases as PC
 from workloads import random_case
 
 pytestmark = pytest.mark.gpu
@@ -52,16 +53,15 @@ def _check(m, case, threshold, x_bits=None):
     assert np.array_equal(used_SCB.cpu().numpy(), SCB), "SCB"
     assert np.array_equal(m.state.idx.cpu().numpy(), r["idx"]), "state.idx"
     assert np.array_equal(m.state.ws.CA.cpu().numpy(), r["CA"]), "CA"
-    err = normwise_rel(bits_of(out), r["out64"], case.dtype)
-    assert err <= OUT_TOL, f"out normwise rel err {err}"
+    assert_out(bits_of(out), r, case.dtype)
     return out, r
 
 
 @pytest.mark.parametrize("dtype", ["f16", "bf16"])
 @pytest.mark.parametrize("has_fp16_weights", [False, True])
-@pytest.mark.parametrize("threshold", [0.0, 6.0])
+@pytest.mark.parametrize("threshold", PC.MODULE_THRESHOLDS)
 def test_module_matches_oracle(dtype, has_fp16_weights, threshold):
-    case = random_case(37, 136, 72, dtype=dtype, seed=91, n_out=3)
+    case = PC.module_case(dtype)
     m = _module_from_case(case, has_fp16_weights, threshold)
     assert m.is_quantized == (not has_fp16_weights)
     if not has_fp16_weights:
@@ -87,6 +87,7 @@ def test_conversion_example_sequential():
         assert np.array_equal(layer.weight.CB.cpu().numpy(), CB)
         assert np.array_equal(layer.weight.SCB.cpu().numpy(), SCB)
         rec = layer.recovered_weight().float().cpu().numpy()
+        np.testing.assert_array_equal(rec, O.recover_weight(CB, SCB, "f16"))
         assert np.all(np.abs(rec - ref.weight.detach().float().numpy()) <= SCB[:, None] / 254 + 1e-3)
     x = torch.randn(8, 64, dtype=torch.float16)
     x[:, 5] *= 20
@@ -101,7 +102,7 @@ def test_conversion_example_sequential():
         bias = ref.bias.detach().view(torch.int16).numpy().view(np.uint16)
         r = O.linear_forward(inp, "f16", CB, SCB, bias, 6.0)
         got = layer(to_dev(inp, "f16"))
-        assert normwise_rel(bits_of(got), r["out64"], "f16") <= OUT_TOL
+        assert_out(bits_of(got), r, "f16")
     assert 5 in int8_model[0].state.idx.cpu().tolist()
     assert y.shape == (8, 64)
 
@@ -129,7 +130,7 @@ def test_issue_state_idx_all_columns():
 
 def test_fp16_weights_requantised_every_forward():
     import torch
-    case = random_case(9, 64, 24, seed=5, n_out=2)
+    case = PC.module_requant_case()
     m = _module_from_case(case, True, 6.0)
     _check(m, case, 6.0)
     with torch.no_grad():
@@ -161,7 +162,7 @@ def test_persistence_round_trip_is_bit_identical(tmp_path):
 
 def test_leading_dims_and_workspace_reuse():
     import torch
-    case = random_case(24, 64, 16, seed=6, n_out=1)
+    case = PC.module_reuse_case()
     m = _module_from_case(case, False, 6.0)
     x = to_dev(case.X, "f16").reshape(2, 3, 4, 64)
     with torch.no_grad():

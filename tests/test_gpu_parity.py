@@ -8,8 +8,9 @@ import numpy as np
 import pytest
 
 import oracle as O
-from tests.gpu_helpers import OUT_TOL, bits_of, normwise_rel, to_dev
-from workloads import config_case, make_case, random_case
+from tests import parity_cases as PC
+from tests.gpu_helpers import assert_out, bits_of, to_dev
+from workloads import config_case, random_case
 
 pytestmark = pytest.mark.gpu
 
@@ -50,8 +51,7 @@ def _check_full(case, threshold=None):
     assert np.array_equal(g["SCA"], r["SCA"]), "SCA"
     assert np.array_equal(g["CA"], r["CA"]), "CA"
     assert np.array_equal(g["acc"], r["acc"]), "acc"
-    err = normwise_rel(g["out"], r["out64"], case.dtype)
-    assert err <= OUT_TOL, f"out normwise rel err {err}"
+    assert_out(g["out"], r, case.dtype)
     return g, r
 
 
@@ -61,35 +61,15 @@ def test_tiny_config():
     assert g["idx"].tolist() == [3, 17]
 
 
-SHAPES = [
-    (1, 64, 64), (3, 24, 5), (8, 8, 4), (16, 4096, 130), (17, 520, 300), (33, 136, 65),
-    (100, 264, 257), (130, 1000, 129), (257, 512, 513), (300, 136, 40), (64, 8, 1), (5, 100, 7),
-    (2, 17, 3), (40, 37, 11), (600, 640, 520),
-    # T, N >= 512 with fewer than 128 tiles of 256 x 256: small tiles
-    (600, 768, 520), (513, 256, 777), (512, 512, 512), (530, 520, 515), (515, 100, 520),
-    # large tiles (at least 128 of them): 128-byte steps in pairs (K % 256 ==
-    # 0; two steps only at K = 256), 64-byte steps (K % 64 == 0), register
-    # staging (8-byte, 4-byte loads), each with ragged T and N tails
-    (2000, 768, 4100), (2050, 256, 4097), (2048, 576, 4096), (2000, 520, 4100), (2001, 100, 4100),
-    # 16 < T <= 64 with K % 16 == 0 and N <= 4096 (K <= 4096 past 32 tokens): the
-    # weight-streaming kernel, 2 or 4 token blocks; otherwise the tiles
-    (17, 512, 300), (32, 4096, 520), (33, 256, 65), (48, 2048, 1000), (64, 1024, 130),
-    (65, 512, 100), (128, 4096, 260), (100, 1040, 33),
-    # T < 512 with at least 256 tiles of 128 x 128: the 128 x 128 tile path (others take 64 x 64)
-    (300, 256, 11000),
-]
-
-
 @pytest.mark.parametrize("dtype", ["f16", "bf16"])
-@pytest.mark.parametrize("T,K,N", SHAPES)
+@pytest.mark.parametrize("T,K,N", PC.SHAPES)
 def test_random_shapes(T, K, N, dtype):
-    case = random_case(T, K, N, dtype=dtype, seed=T * 7 + K * 3 + N, n_out=min(3, K))
-    _check_full(case)
+    _check_full(PC.shape_case(T, K, N, dtype))
 
 
-@pytest.mark.parametrize("tau", [0.0, -1.0, float("inf"), 0.1, 2.5])
+@pytest.mark.parametrize("tau", PC.THRESHOLDS)
 def test_thresholds(tau):
-    case = random_case(40, 200, 70, seed=11, n_out=4)
+    case = PC.threshold_case()
     g, r = _check_full(case, tau)
     if tau <= 0 or tau == float("inf"):
         assert g["n"] == 0
@@ -99,10 +79,7 @@ def test_thresholds(tau):
 
 def test_issue_repro_shape_all_columns():
     """x[2, 8] with threshold 0.1 flags all 8 columns (state.idx = [0..7])."""
-    rng = np.random.default_rng(1609)
-    x = rng.standard_normal((2, 8)).astype(np.float32)
-    case = make_case("issue", 2, 8, 4, n_out=0, bias="normal", threshold=0.1, seed=1609)
-    case.X = x.astype(np.float16).view(np.uint16)
+    case = PC.issue_case()
     g, r = _check_full(case)
     assert g["idx"].tolist() == list(range(8))
     assert not g["CA"].any() and not g["SCA"].any() and not g["acc"].any()
@@ -110,26 +87,13 @@ def test_issue_repro_shape_all_columns():
 
 def test_threshold_edge_exact_value():
     """A column whose largest magnitude is exactly the threshold is not flagged."""
-    case = random_case(12, 64, 16, seed=4, n_out=0)
-    x = O.decode_bits(case.X, "f16").copy()
-    x[:, 5] = 0.5
-    x[3, 5] = 6.0
-    x[:, 9] = 0.25
-    x[7, 9] = -6.00390625
-    case.X = x.astype(np.float16).view(np.uint16)
+    case = PC.threshold_edge_case()
     g, r = _check_full(case, 6.0)
     assert g["idx"].tolist() == [9]
 
 
 def test_zero_rows_and_columns():
-    case = random_case(20, 96, 33, seed=8, n_out=2)
-    x = O.decode_bits(case.X, "f16").copy()
-    x[4] = 0.0          # a zero row: SCA = 0, CA = 0
-    x[:, 50] = 0.0      # a zero column
-    case.X = x.astype(np.float16).view(np.uint16)
-    w = O.decode_bits(case.W, "f16").copy()
-    w[3] = 0.0          # a zero weight row: SCB = 0
-    case.W = w.astype(np.float16).view(np.uint16)
+    case = PC.zero_rows_case()
     g, r = _check_full(case)
     assert g["SCA"][4] == 0 and not g["CA"][4].any()
     assert g["SCB"][3] == 0
@@ -196,32 +160,25 @@ def test_leading_dims_flatten():
     assert torch.equal(out3.reshape(30, 24), out2)
 
 
-SMALL_T = [(1, 64, 64), (3, 48, 5), (16, 4096, 130), (8, 8192, 40), (16, 8448, 33), (5, 1024, 4097),
-           (16, 256, 16), (2, 512, 3000), (11, 2048, 1000), (16, 64, 8192)]
-
-
 @pytest.mark.parametrize("fused", ["1", "0"])
 @pytest.mark.parametrize("dtype", ["f16", "bf16"])
-@pytest.mark.parametrize("T,K,N", SMALL_T)
+@pytest.mark.parametrize("T,K,N", PC.SMALL_T)
 def test_small_T_both_decode_paths(T, K, N, dtype, fused, monkeypatch):
     """T <= 16 runs the single-launch path by default; LLI8_FUSED_DECODE=0 selects the
     multi-kernel path.  Both must match the oracle."""
     monkeypatch.setenv("LLI8_FUSED_DECODE", fused)
-    case = random_case(T, K, N, dtype=dtype, seed=T + K + N, n_out=min(4, K))
-    _check_full(case)
+    _check_full(PC.small_t_case(T, K, N, dtype))
 
 
-@pytest.mark.parametrize("tau", [0.0, 0.1, 2.0, float("inf")])
+@pytest.mark.parametrize("tau", PC.FUSED_THRESHOLDS)
 def test_fused_decode_thresholds(tau):
     """Degenerate and dense thresholds on the single-launch path (T <= 16)."""
-    case = random_case(16, 1024, 512, seed=77, n_out=3)
-    _check_full(case, tau)
+    _check_full(PC.fused_threshold_case(), tau)
 
 
 def test_fused_decode_many_blocks_per_workgroup():
     """N well beyond one 16-feature block per CU: each workgroup walks several blocks."""
-    case = random_case(7, 512, 16 * 256 * 3 + 5, seed=78, n_out=2)
-    _check_full(case)
+    _check_full(PC.fused_many_blocks_case())
 
 
 @pytest.mark.parametrize("room_chunks", ["full", 0, 1])
@@ -231,12 +188,12 @@ def test_recovered_outlier_weights_scratch_sizes(room_chunks):
     gives the oracle's results (here 70 outlier columns: three chunks)."""
     B = _lib()
     import torch
-    case = random_case(300, 512, 260, seed=31, n_out=70)
+    case = PC.scratch_sizes_case()
     X = to_dev(case.X, case.dtype)
     W = to_dev(case.W, case.dtype)
     CB, SCB = B.lli8_quant_weight_rowwise(W)
     if room_chunks == "full":
-        nbytes = None
+        nbytes = "full"
     else:
         nbytes = B.lli8_scratch_bytes(case.T, case.K) + room_chunks * case.N * 64
     ws = B.Workspace(case.T, case.K, case.N, X.dtype, X.device, want_acc=True, scratch_bytes=nbytes)
@@ -246,13 +203,13 @@ def test_recovered_outlier_weights_scratch_sizes(room_chunks):
     r = O.linear_forward(case.X, case.dtype, rCB, rSCB, None, case.threshold)
     assert int(ws.n_idx.item()) == r["idx"].size == 70
     assert np.array_equal(ws.acc.cpu().numpy(), r["acc"])
-    assert normwise_rel(bits_of(out), r["out64"], case.dtype) <= OUT_TOL
+    assert_out(bits_of(out), r, case.dtype)
 
 
 def test_every_column_an_outlier_skips_nothing_it_needs():
     """All K columns flagged (tiny threshold): the int8 product is skipped and
     the output is the 16-bit product alone."""
-    case = random_case(290, 256, 300, seed=33, n_out=0)
+    case = PC.every_column_case()
     g, r = _check_full(case, 0.01)
     assert g["n"] == case.K
     assert not g["acc"].any()
@@ -291,18 +248,9 @@ def test_graph_replays_match_eager(T, K, N):
         assert torch.equal(got_b, ref_b)
 
 
-@pytest.mark.parametrize("T,K,N,n_out,tau,dtype", [
-    # whole 256 x 256 tiles, more tiles than compute units: workgroups walk
-    # several tiles each, the next tile's first steps loaded during the
-    # current tile's epilogue when the outlier columns fit in registers
-    (2048, 256, 8448, 3, 6.0, "f16"),      # two K steps per tile, one chunk
-    (2048, 512, 8448, 100, 6.0, "bf16"),   # four chunks: still from registers
-    (2048, 512, 8448, 150, 6.0, "f16"),    # five chunks: staged through LDS, no cross-tile loads
-    (2048, 256, 8448, 0, 0.01, "bf16"),    # every column an outlier: no int8 product at all
-    (2048, 768, 8448, 2, 0.0, "f16"),      # threshold off: no outlier columns
-])
+@pytest.mark.parametrize("T,K,N,n_out,tau,dtype", PC.PERSISTENT)
 def test_persistent_tiles(T, K, N, n_out, tau, dtype):
-    case = random_case(T, K, N, dtype=dtype, seed=T + K + N + n_out, n_out=n_out)
+    case = PC.persistent_case(T, K, N, n_out, tau, dtype)
     g, r = _check_full(case, tau)
     if tau == 0.0:
         assert g["n"] == 0
@@ -311,15 +259,9 @@ def test_persistent_tiles(T, K, N, n_out, tau, dtype):
 
 
 @pytest.mark.parametrize("dtype", ["f16", "bf16"])
-@pytest.mark.parametrize("T,K,N,n_out,tau", [
-    (600, 512, 520, 150, 6.0),    # 5 outlier chunks: 4 through the 2-slot pipeline, 1 through the ring
-    (520, 768, 530, 0, 0.01),     # every column an outlier: 24 chunks, all through the pipeline
-    (512, 1024, 512, 260, 6.0),   # 9 chunks: 8 + 1
-    # the same on 256 x 256 tiles (at least 128 of them)
-    (2000, 512, 4100, 150, 6.0), (2000, 768, 4100, 0, 0.01), (2000, 1024, 4100, 260, 6.0),
-])
+@pytest.mark.parametrize("T,K,N,n_out,tau", PC.MANY_CHUNKS)
 def test_many_outlier_chunks_large_tiles(T, K, N, n_out, tau, dtype):
-    case = random_case(T, K, N, dtype=dtype, seed=T + K + n_out, n_out=n_out)
+    case = PC.many_chunks_case(T, K, N, n_out, tau, dtype)
     g, r = _check_full(case, tau)
     assert g["n"] >= min(n_out, K) and (tau > 0.1 or g["n"] == K)
 
@@ -346,7 +288,8 @@ def test_recovered_weights_bit_exact(dtype, every_column):
         Wb = O.round_to_dtype_bits(vals, dtype)
     CB, SCB = B.lli8_quant_weight_rowwise(to_dev(Wb, dtype))
     tau = 1e-30 if every_column else 6.0
-    _, ws = B.lli8_int8_linear(to_dev(case.X, dtype), CB, SCB, None, tau)
+    ws = B.Workspace(T, K, N, None, CB.device, scratch_bytes="full")
+    _, ws = B.lli8_int8_linear(to_dev(case.X, dtype), CB, SCB, None, tau, ws=ws)
     torch.cuda.synchronize()
     n = int(ws.n_idx.item())
     assert n == K if every_column else n >= 40
@@ -360,50 +303,13 @@ def test_recovered_weights_bit_exact(dtype, every_column):
     assert not got[:, n:].any()
 
 
-def _sweep_case(seed):
-    """A seeded random shape across the launch routes: whole 256 x 256 tiles
-    (persistent kernel), few rows (strip scan, weight streaming, small tiles),
-    ragged large shapes and small ones; either dtype, a few outlier counts and
-    thresholds."""
-    rng = np.random.default_rng(1000 + seed)
-    kind = seed % 4
-    if kind == 0:
-        T, N, K = 256 * int(rng.integers(2, 9)), 256 * int(rng.integers(2, 40)), 256 * int(rng.integers(1, 9))
-    elif kind == 1:
-        T, N, K = int(rng.integers(1, 300)), int(rng.integers(1, 3000)), 8 * int(rng.integers(1, 600))
-    elif kind == 2:
-        T, N, K = int(rng.integers(500, 1500)), int(rng.integers(500, 3000)), int(rng.integers(1, 1200))
-    else:
-        T, N, K = int(rng.integers(1, 200)), int(rng.integers(1, 500)), int(rng.integers(1, 700))
-    if T * N * K > 3e8:  # keep the oracle quick
-        if kind == 0:
-            N = max(256, int(3e8 // (T * K)) // 256 * 256)
-        else:
-            K = max(1, int(3e8 // (T * N)))
-    dtype = "f16" if rng.integers(0, 2) == 0 else "bf16"
-    n_out = int(rng.choice([0, 1, 3, 17, 40, 150]))
-    tau = float(rng.choice([6.0, 6.0, 6.0, 2.5, 0.0]))
-    return random_case(T, K, N, dtype=dtype, seed=int(rng.integers(0, 1 << 30)), n_out=min(n_out, K)), tau
-
-
-@pytest.mark.parametrize("seed", range(48))
+@pytest.mark.parametrize("seed", PC.SWEEP_SEEDS)
 def test_random_sweep(seed):
-    case, tau = _sweep_case(seed)
+    case, tau = PC.sweep_case(seed)
     _check_full(case, tau)
 
 
-# Few rows (T <= 32, K % 8 == 0, K <= 4096): the scan and the quantiser run
-# as one launch; each register depth (8, 16, 24, 32 rows), K not a multiple
-# of 16 or 32, either dtype, thresholds that flag nothing; and a few shapes
-# just past it, on the two-launch split.
-SPLIT_SMALL = [(1, 8, 5, "f16", 6.0), (7, 40, 33, "bf16", 6.0), (8, 4096, 64, "f16", 6.0),
-               (12, 1000, 70, "f16", 2.5), (17, 4088, 100, "bf16", 6.0), (24, 4096, 300, "f16", 6.0),
-               (25, 520, 48, "bf16", 0.0), (32, 4096, 256, "f16", 6.0), (32, 2056, 40, "bf16", float("inf")),
-               (31, 96, 17, "f16", 1.0), (33, 4096, 64, "f16", 6.0), (47, 1032, 20, "bf16", 6.0),
-               (64, 4096, 128, "f16", 6.0), (64, 8, 9, "bf16", 0.0)]
-
-
-@pytest.mark.parametrize("T,K,N,dtype,tau", SPLIT_SMALL)
+@pytest.mark.parametrize("T,K,N,dtype,tau", PC.SPLIT_SMALL)
 def test_few_rows_one_launch_split(T, K, N, dtype, tau, monkeypatch):
     """Outputs of the one-launch split (also with the fused decode off, so T <= 16
     takes it inside lli8_int8_linear) and the gathered outlier columns it leaves
@@ -411,7 +317,7 @@ def test_few_rows_one_launch_split(T, K, N, dtype, tau, monkeypatch):
     B = _lib()
     import torch
     monkeypatch.setenv("LLI8_FUSED_DECODE", "0")
-    case = random_case(T, K, N, dtype=dtype, seed=500 + T + K, n_out=min(6, K))
+    case = PC.split_small_case(T, K, N, dtype)
     g, r = _check_full(case, tau)
     CA, SCA, bitmap, idx, n_idx = B.lli8_quant_rowwise_outliers(to_dev(case.X, dtype), tau)
     n = int(n_idx.item())
@@ -430,3 +336,26 @@ def test_few_rows_one_launch_split(T, K, N, dtype, tau, monkeypatch):
         got = xo.transpose(1, 0, 2).reshape(T, chunks * 32)
         assert np.array_equal(got[:, :n], case.X[:, r["idx"]])
         assert not got[:, n:].any()
+
+
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+@pytest.mark.parametrize("N,K", [(300, 512), (7, 13), (1, 1), (130, 4104), (64, 8)])
+def test_recover_weight_entry_point(N, K, dtype):
+    """lli8_recover_weight gives dtype(fl32(fl32(CB * SCB) / 127)) bit for bit,
+    including row scales far outside the range where the division is taken
+    by multiply-and-correct (bf16 rows scaled by 1e-34 and 1e34)."""
+    B = _lib()
+    import torch
+    case = random_case(1, K, N, dtype=dtype, seed=N + K, n_out=0)
+    Wb = case.W
+    if dtype == "bf16":
+        vals = O.decode_bits(Wb, dtype).astype(np.float64)
+        vals[0::7] *= 1e-34
+        vals[3::11] *= 1e34
+        Wb = O.round_to_dtype_bits(vals, dtype)
+    CB, SCB = B.lli8_quant_weight_rowwise(to_dev(Wb, dtype))
+    tdt = torch.float16 if dtype == "f16" else torch.bfloat16
+    W = B.lli8_recover_weight(CB, SCB, dtype=tdt)
+    torch.cuda.synchronize()
+    ref = O.recover_weight(CB.cpu().numpy(), SCB.cpu().numpy(), dtype)
+    np.testing.assert_array_equal(O.decode_bits(bits_of(W), dtype).astype(np.float64), ref)
