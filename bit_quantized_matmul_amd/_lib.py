@@ -77,6 +77,10 @@ def lib() -> ctypes.CDLL:
     L.lli8_int8_linear.restype = i32
     L.lli8_quant_vectorwise.argtypes = [vp, i64, i64, i32, i32, i32, vp, vp, vp, vp]
     L.lli8_quant_vectorwise.restype = i32
+    L.lli8_int8_linear_noalloc.argtypes = [vp, i64, i64, i64, i32, vp, vp, vp, f32, vp, vp]
+    L.lli8_int8_linear_noalloc.restype = i32
+    L.lli8_noalloc_scratch_bytes.argtypes = []
+    L.lli8_noalloc_scratch_bytes.restype = ctypes.c_size_t
     L.lli8_recover_weight.argtypes = [vp, vp, i64, i64, i32, vp, vp]
     L.lli8_recover_weight.restype = i32
     L.lli8_workspace_bytes.argtypes = [i64, i64, i64, i32]
@@ -377,3 +381,32 @@ def lli8_int8_linear(X, CB, SCB, bias=None, threshold: float = 6.0, out=None,
                                   float(threshold), _ptr(out), ctypes.byref(ws._struct),
                                   _stream(X.device, stream)))
     return (out if X.dim() == 2 else out.reshape(*X.shape[:-1], N)), ws
+
+
+def lli8_int8_linear_noalloc(X, CB, SCB, bias=None, threshold: float = 6.0, out=None, stream=None):
+    """The forward of lli8_int8_linear with the workspace in the library's
+    fixed per-GPU array (lli8_int8_linear_noalloc): the C call allocates
+    nothing.  Pass `out` to keep this binding from allocating it.  Calls that
+    overlap on one GPU race on the shared array."""
+    torch = _torch()
+    dev = _gpu(X, "X")
+    X2 = X if X.dim() == 2 else X.reshape(-1, X.shape[-1])
+    T, K = X2.shape
+    if CB.dim() != 2 or CB.shape[1] != K:
+        raise ValueError(f"CB has shape {tuple(CB.shape)}, X has K={K}")
+    N = CB.shape[0]
+    _arg(CB, "CB", dev, torch.int8, N * K)
+    _arg(SCB, "SCB", dev, torch.float32, N)
+    if bias is not None:
+        _arg(bias, "bias", dev, X.dtype, N)
+    if out is None:
+        out = torch.empty((T, N), dtype=X.dtype, device=dev)
+    else:
+        _arg(out, "out", dev, X.dtype, T * N)
+    _check(lib().lli8_int8_linear_noalloc(_ptr(X2), T, K, N, _dt(X2), _ptr(CB), _ptr(SCB), _ptr(bias),
+                                          float(threshold), _ptr(out), _stream(dev, stream)))
+    return out if X.dim() == 2 else out.reshape(*X.shape[:-1], N)
+
+
+def lli8_noalloc_scratch_bytes() -> int:
+    return int(lib().lli8_noalloc_scratch_bytes())

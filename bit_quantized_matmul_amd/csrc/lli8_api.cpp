@@ -173,6 +173,28 @@ Carve carve_layout(int64_t T, int64_t K, int64_t N) {
 
 }  // namespace
 
+namespace lli8 {
+
+lli8_status_t check_linear_args(const void* X, int64_t T, int64_t K, int64_t N, lli8_dtype_t dtype,
+                                const int8_t* CB, const float* SCB, const void* bias, float threshold,
+                                const void* out) {
+  TRY(check_dtype(dtype));
+  TRY(check_sizes(T, K, N));
+  if (isnan(threshold)) return fail(LLI8_ERR_THRESHOLD, "threshold is NaN");
+  REQUIRE(CB, "CB");
+  REQUIRE(SCB, "SCB");
+  OPTIONAL(bias, "bias");
+  if (T > 0) {  // with T == 0 nothing of size T is read or written
+    REQUIRE(X, "X");
+    REQUIRE(out, "out");
+  }
+  return LLI8_OK;
+}
+
+lli8_status_t set_error(lli8_status_t st, const char* msg) { return fail(st, "%s", msg); }
+
+}  // namespace lli8
+
 extern "C" {
 
 const char* lli8_version(void) { return "0.1.0"; }
@@ -328,16 +350,9 @@ lli8_status_t lli8_quant_rowwise_outliers(const void* X, int64_t T, int64_t K, l
 lli8_status_t lli8_int8_linear(const void* X, int64_t T, int64_t K, int64_t N, lli8_dtype_t dtype, const int8_t* CB,
                                const float* SCB, const void* bias, float threshold, void* out,
                                const lli8_workspace_t* ws, void* stream) {
-  TRY(check_dtype(dtype));
-  TRY(check_sizes(T, K, N));
-  if (isnan(threshold)) return fail(LLI8_ERR_THRESHOLD, "threshold is NaN");
-  REQUIRE(CB, "CB");
-  REQUIRE(SCB, "SCB");
-  OPTIONAL(bias, "bias");
+  TRY(lli8::check_linear_args(X, T, K, N, dtype, CB, SCB, bias, threshold, out));
   if (ws == nullptr) return fail(LLI8_ERR_NULL, "workspace is NULL");
   if (T > 0) {  // with T == 0 nothing of size T is read or written
-    REQUIRE(X, "X");
-    REQUIRE(out, "out");
     REQUIRE(ws->CA, "ws->CA");
     REQUIRE(ws->SCA, "ws->SCA");
   }

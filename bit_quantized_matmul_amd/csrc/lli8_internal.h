@@ -4,7 +4,17 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "../../include/lli8.h"
+
 namespace lli8 {
+
+// Validation of lli8_int8_linear's arguments other than the workspace
+// (records the message lli8_last_error returns).
+lli8_status_t check_linear_args(const void* X, int64_t T, int64_t K, int64_t N, lli8_dtype_t dtype,
+                                const int8_t* CB, const float* SCB, const void* bias, float threshold,
+                                const void* out);
+// Records msg as this thread's lli8_last_error and returns st.
+lli8_status_t set_error(lli8_status_t st, const char* msg);
 
 hipError_t launch_fill_u32(uint32_t* p, int64_t n, uint32_t v, hipStream_t s);
 

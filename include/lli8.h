@@ -173,6 +173,33 @@ lli8_status_t lli8_int8_linear(const void* X, int64_t T, int64_t K, int64_t N,
                                const lli8_workspace_t* ws, void* stream);
 
 /*
+ * lli8_int8_linear for callers that cannot allocate device memory: code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * allocation.  The same forward, the same kernels and the same output as
+ * lli8_int8_linear, with every workspace buffer (CA, SCA, bitmap, idx,
+ * n_idx and the scratch, laid out as lli8_workspace_carve lays them out) in
+ * a fixed device array of LLI8_NOALLOC_SCRATCH_BYTES bytes that the library
+ * holds on each GPU it runs on until the process ends.  The caller passes
+ * inputs and outputs as for lli8_int8_linear; no int32 accumulators are
+ * written.  The call allocates nothing and frees nothing (the array's device
+ * address is looked up once per device, on the first call there).
+ *   - Sizes whose lli8_workspace_bytes(T, K, N, dtype) exceeds the array
+ *     (e.g. 4096 tokens at K = 12288) are rejected with LLI8_ERR_UNSUPPORTED
+ *     before anything is enqueued; 4096 x 4096 -> 11008 fits.
+ *   - Every call on one GPU shares that GPU's array, which keeps the last
+ *     call's contents: calls that overlap on one GPU (other streams, other
+ *     threads) race and must be serialised by the caller.
+ *   - Other errors as lli8_int8_linear.
+ */
+#define LLI8_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+lli8_status_t lli8_int8_linear_noalloc(const void* X, int64_t T, int64_t K, int64_t N,
+                                       lli8_dtype_t dtype, const int8_t* CB, const float* SCB,
+                                       const void* bias, float threshold, void* out, void* stream);
+
+/* LLI8_NOALLOC_SCRATCH_BYTES, for bindings that cannot read the macro. */
+size_t lli8_noalloc_scratch_bytes(void);
+
+/*
  * Weight recovery, "Hugging Face integrates LLM.int8() ...", section
  * "Integration into transformers": the weight the int8 codes stand for is
  * (CB * SCB) / 127.  Evaluated left to right in fp32 and rounded once to the

@@ -223,6 +223,16 @@ def test_binding_rejects_host_and_mismatched_tensors():
         Lm._arg(torch.zeros(6, device="meta"), "bias", dev, torch.float32, 6)
 
 
+def test_package_exports_every_binding_function():
+    import bit_quantized_matmul_amd as B
+    from bit_quantized_matmul_amd import _lib as L
+    public = [n for n in dir(L) if n.startswith("lli8_") and callable(getattr(L, n))]
+    assert public
+    for n in public:
+        assert getattr(B, n, None) is getattr(L, n), f"{n} is not exported by the package"
+        assert n in B.__all__
+
+
 def test_product_path_has_no_cpu_fallback():
     """The package's compute entry points go only through the HIP library."""
     pkg = os.path.join(ROOT, "bit_quantized_matmul_amd")
