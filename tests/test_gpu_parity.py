@@ -266,6 +266,39 @@ def test_many_outlier_chunks_large_tiles(T, K, N, n_out, tau, dtype):
     assert g["n"] >= min(n_out, K) and (tau > 0.1 or g["n"] == K)
 
 
+@pytest.mark.parametrize("n_out", [1, 31, 32, 33, 100])
+def test_persistent_route_recovered_outlier_weights(n_out):
+    """On the persistent 256 x 256 route (up to four outlier chunks kept in
+    the epilogue's registers) the recovered outlier weights in scratch are
+    bit for bit the oracle's dtype(fl32(fl32(CB * SCB) / 127)), chunk padding
+    zeroed, whatever the scratch held before; the forward matches the
+    oracle."""
+    B = _lib()
+    import torch
+    T, K, N = 2048, 512, 4096  # 8 x 16 tiles of 256 x 256: the persistent kernel
+    case = random_case(T, K, N, dtype="bf16", seed=600 + n_out, n_out=n_out)
+    X = to_dev(case.X, "bf16")
+    CB, SCB = B.lli8_quant_weight_rowwise(to_dev(case.W, "bf16"))
+    ws = B.Workspace(T, K, N, None, X.device, want_acc=True)
+    ws.scratch.fill_(0xFF)  # whatever the scratch held before
+    out, ws = B.lli8_int8_linear(X, CB, SCB, to_dev(case.bias, "bf16"), case.threshold, ws=ws, want_acc=True)
+    torch.cuda.synchronize()
+    n = int(ws.n_idx.item())
+    assert n >= n_out and (n + 31) // 32 <= 4
+    idx = ws.idx[:n].cpu().numpy()
+    chunks = (n + 31) // 32
+    xb = B.lli8_scratch_bytes(T, K)
+    wo = ws.scratch[xb:xb + chunks * N * 64].cpu().numpy().view(np.uint16).reshape(chunks, N, 32)
+    got = O.decode_bits(wo.transpose(1, 0, 2).reshape(N, chunks * 32), "bf16").astype(np.float64)
+    ref = O.recover_weight(CB.cpu().numpy()[:, idx], SCB.cpu().numpy(), "bf16")
+    np.testing.assert_array_equal(got[:, :n], ref)
+    assert not got[:, n:].any()
+    rCB, rSCB = O.quantize_weight_bits(case.W, "bf16")
+    r = O.linear_forward(case.X, "bf16", rCB, rSCB, case.bias, case.threshold)
+    assert np.array_equal(ws.acc.cpu().numpy(), r["acc"])
+    assert_out(bits_of(out), r, "bf16")
+
+
 @pytest.mark.parametrize("every_column", [False, True])
 @pytest.mark.parametrize("dtype", ["f16", "bf16"])
 def test_recovered_weights_bit_exact(dtype, every_column):

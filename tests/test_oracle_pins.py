@@ -71,6 +71,56 @@ def test_weight_recovery_bound(dtype):
     assert np.all(np.abs(CB).max(axis=1) == 127)
 
 
+def _fl32(q):
+    """Exact rational -> the nearest float32 value (ties to even), as a Fraction."""
+    from fractions import Fraction
+    if q == 0:
+        return Fraction(0)
+    sgn = -1 if q < 0 else 1
+    a = abs(q)
+    e = a.numerator.bit_length() - a.denominator.bit_length()
+    if Fraction(2) ** e > a:
+        e -= 1
+    e = max(e, -126)                      # subnormal spacing below 2^-126
+    ulp = Fraction(2) ** (e - 23)
+    m = a / ulp
+    fl = m.numerator // m.denominator
+    rem = m - fl
+    if rem > Fraction(1, 2) or (rem == Fraction(1, 2) and fl % 2 == 1):
+        fl += 1
+    return sgn * fl * ulp
+
+
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+def test_weight_recovery_rounding_order_exact(dtype):
+    """Integration into transformers prints the recovery as (CB * SCB) / 127:
+    the product first, then the division, each rounded to float32, then one
+    rounding to the 16-bit dtype.  Exact rational arithmetic with explicit
+    round-to-nearest-even reproduces recover_weight bit for bit, and the pin
+    has teeth: on these inputs dividing the scale first
+    (CB * fl32(SCB / 127)) gives different float32 values."""
+    from fractions import Fraction
+    rng = np.random.default_rng(11)
+    SCB = (rng.uniform(0.01, 3.0, size=64) * rng.choice([1e-3, 1.0, 1e3], size=64)).astype(np.float32)
+    CB = rng.integers(-127, 128, size=(64, 16)).astype(np.int8)
+    got = O.recover_weight(CB, SCB, dtype)
+    differs = 0
+    for n in range(64):
+        s = Fraction(float(SCB[n]))
+        for k in range(16):
+            c = int(CB[n, k])
+            v = _fl32(_fl32(c * s) / 127)
+            ref16 = O.decode_bits(O.round_to_dtype_bits(np.float64(v), dtype), dtype)
+            assert got[n, k] == float(ref16), (n, k)
+            differs += v != _fl32(c * _fl32(s / 127))
+    assert differs > 0
+    # a scale of 127 * 2^j recovers the codes exactly scaled by 2^j
+    for j in (-6, 0, 5):
+        sc = np.full(4, np.float32(127.0 * 2.0 ** j))
+        cb = np.array([[-127, -1, 0, 1, 64, 127]] * 4, dtype=np.int8)
+        np.testing.assert_array_equal(O.recover_weight(cb, sc, dtype), cb.astype(np.float64) * 2.0 ** j)
+
+
 # ---------------------------------------------------------------- P-3 -----
 def test_threshold_zero_is_no_decomposition():
     """Class Linear8bitLt: threshold defaults to 0.0 and the plain int8 examples use no
