@@ -93,9 +93,10 @@ def _fl32(q):
 
 @pytest.mark.parametrize("dtype", ["f16", "bf16"])
 def test_weight_recovery_rounding_order_exact(dtype):
-    """Integration into transformers prints the recovery as (CB * SCB) / 127:
-    the product first, then the division, each rounded to float32, then one
-    rounding to the 16-bit dtype.  Exact rational arithmetic with explicit
+    """The Hugging Face integration page ("Integration into transformers")
+    writes the recovery as (CB * SCB) / 127, read literally: the product
+    first, then the division, each rounded to float32, then one rounding to
+    the 16-bit dtype.  Exact rational arithmetic with explicit
     round-to-nearest-even reproduces recover_weight bit for bit, and the pin
     has teeth: on these inputs dividing the scale first
     (CB * fl32(SCB / 127)) gives different float32 values."""
