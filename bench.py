@@ -25,6 +25,9 @@ stream different weights -- so no step finds its operands in cache.  The K
 steps run back to back between one pair of HIP events on the library's
 stream; ms_per_step is the elapsed time divided by K.  (A per-step event pair
 would add the ~6 us floor of an event-bracketed launch on this platform.)
+The same number of steps then runs again in up to 10 blocks with one event
+pair each; "dispersion" gives the 10th, 50th and 90th percentiles of the
+blocks' per-step times.
 
 Prints one JSON line on stdout.  `value` is the effective throughput
 2*T*N*K / t in TOPS.  `roofline` describes the kernel with the largest average
@@ -380,6 +383,23 @@ def measure(name, case, args):
     t_wall = time.perf_counter() - t_wall
     ms = e0.elapsed_time(e1) / args.steps
 
+    # dispersion: the same number of steps again, in blocks with one event
+    # pair each (an event pair around every step would add more than a
+    # decode step costs), reported as percentiles of the per-block means
+    nb = min(10, args.steps)
+    per = max(1, args.steps // nb)
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(nb + 1)]
+    evs[0].record()
+    for b in range(nb):
+        for j in range(per):
+            step(args.warmup + args.steps + b * per + j)
+        evs[b + 1].record()
+    torch.cuda.synchronize()
+    blocks = [evs[b].elapsed_time(evs[b + 1]) / per for b in range(nb)]
+    p10, p50, p90 = (float(v) for v in np.percentile(blocks, [10, 50, 90]))
+    dispersion = {"blocks": nb, "steps_per_block": per, "ms_per_step_p10": round(p10, 5),
+                  "ms_per_step_median": round(p50, 5), "ms_per_step_p90": round(p90, 5)}
+
     # per-kernel durations: a second pass with events around each kernel
     # (through the binding: events cannot be recorded inside a replayed graph)
     B.lli8_trace_enable(True)
@@ -429,6 +449,7 @@ def measure(name, case, args):
                    "kernels_ms": {k: round(v, 5) for k, v in avg.items()},
                    "timed_wall_s": round(t_wall, 3)},
         "roofline": roof,
+        "dispersion": dispersion,
     }
     return line
 
@@ -467,7 +488,7 @@ def main():
         extra[w] = {"value": sub["value"], "unit": sub["unit"], "ms_per_step": sub["ms_per_step"],
                     "T": c["T"], "K": c["K"], "N": c["N"], "n_idx": c["n_idx"],
                     "step_hbm_frac": c["step_hbm_frac"], "kernels_ms": c["kernels_ms"],
-                    "roofline": sub["roofline"]}
+                    "roofline": sub["roofline"], "dispersion": sub["dispersion"]}
     if extra:
         line["workloads"] = extra
     torch.cuda.empty_cache()
