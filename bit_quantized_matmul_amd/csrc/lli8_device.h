@@ -111,7 +111,10 @@ template <int DT>
 __device__ __forceinline__ uint32_t code_pair16(uint32_t x, float s) {
   const int mlo = cvt_rpi(scaled_abs<DT>(x & 0xFFFFu, s));
   const int mhi = cvt_rpi(scaled_abs<DT>(x >> 16, s));
-  const i16x2 mag = __builtin_bit_cast(i16x2, (uint32_t)mlo | ((uint32_t)mhi << 16));
+  // the low 16 bits of each: a value of an excluded (outlier) column, scaled
+  // by a row absmax taken without it, can run far past 16 bits, and its code
+  // (discarded later) must not carry into its neighbour's half
+  const i16x2 mag = __builtin_bit_cast(i16x2, __builtin_amdgcn_perm((uint32_t)mhi, (uint32_t)mlo, 0x05040100u));
   const i16x2 neg = __builtin_bit_cast(i16x2, x) >> 15;  // -1 where x < 0
   return __builtin_bit_cast(uint32_t, (i16x2)((mag ^ neg) - neg));
 }

@@ -74,6 +74,31 @@ def zero_rows_case():
     return case
 
 
+# An outlier column beside a kept one, in rows whose kept values are tiny: the
+# outlier's value times the row's scale runs far past 16 bits (60 / 1e-3 x 127),
+# and the discarded code must not reach its neighbour.  One shape per route:
+# fused decode, one-launch split, strip scan, cooperative launch, separate
+# launches (cooperative launch off), any-K quantiser.
+WIDE_RATIO = [(8, 64, 40, "1"), (24, 64, 40, "1"), (100, 64, 40, "1"), (300, 64, 40, "1"), (300, 64, 40, "0"),
+              (300, 66, 40, "1")]
+
+
+def wide_ratio_case(T, K, N, dtype):
+    case = random_case(T, K, N, dtype=dtype, seed=T * 3 + K + N, n_out=0)
+    x = O.decode_bits(case.X, dtype).astype(np.float64)
+    x[1::2] *= 1e-3                      # every other row: kept values around 1e-3
+    for c in (2, 10, K - 2):             # even columns: outliers in every row
+        x[:, c] = np.where(np.arange(T) % 3 == 0, -60.0, 60.0)
+    case.X = _bits(x, dtype)
+    return case
+
+
+def _bits(x, dtype):
+    if dtype == "f16":
+        return x.astype(np.float16).view(np.uint16)
+    return O.round_to_dtype_bits(x, "bf16").astype(np.uint16)
+
+
 SMALL_T = [(1, 64, 64), (3, 48, 5), (16, 4096, 130), (8, 8192, 40), (16, 8448, 33), (5, 1024, 4097),
            (16, 256, 16), (2, 512, 3000), (11, 2048, 1000), (16, 64, 8192)]
 
@@ -266,6 +291,10 @@ def output_checks():
             out.append((f"module-{dt}-{tau}", lambda dt=dt, tau=tau: (module_case(dt), tau), None, None))
     out += [("module_requant", lambda: (module_requant_case(), 6.0), None, None),
             ("module_reuse", lambda: (module_reuse_case(), 6.0), None, None)]
+    for T, K, N, _ in WIDE_RATIO:
+        for dt in ("f16", "bf16"):
+            out.append((f"wide_ratio{T}x{K}x{N}-{dt}", lambda T=T, K=K, N=N, dt=dt: _own(wide_ratio_case(T, K, N, dt)),
+                        None, None))
     for T, K, N in MAX_K_SHAPES:
         out.append((f"maxk{T}x{K}x{N}", lambda T=T, K=K, N=N: _own(max_k_case(T, K, N)), None, None))
     out.append(("large_k_tiles", lambda: _own(large_k_tiles_case(), bias=False), LARGE_K_ROWS, LARGE_K_COLS))

@@ -126,6 +126,17 @@ def test_activation_split_entry_point():
     assert np.array_equal(bitmap.cpu().numpy().view(np.uint32), O.outlier_bitmap(ridx, case.K))
 
 
+@pytest.mark.parametrize("T,K,N,coop", PC.WIDE_RATIO)
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+def test_outlier_far_beyond_16_bits_leaves_its_neighbour(T, K, N, coop, dtype, monkeypatch):
+    """An outlier value up to 4e6 times its row's scale (a row of tiny kept
+    values) beside a kept column, on every activation route: the kept
+    neighbour's code, and everything else, as the oracle's."""
+    monkeypatch.setenv("LLI8_COOP_ACT", coop)
+    g, r = _check_full(PC.wide_ratio_case(T, K, N, dtype))
+    assert g["n"] == 3
+
+
 def test_rounding_halves_on_gpu():
     """Row [127, 2.5, -2.5, 0.5, 1.5, -0.5] codes to [127, 3, -3, 1, 2, -1]."""
     B = _lib()
