@@ -40,8 +40,6 @@ hipError_t launch_quant_act(int dt, const void* X, int64_t T, int64_t K, const u
                             int8_t* CA, float* SCA, int32_t* idx, int32_t* n_idx, void* xo,
                             hipStream_t s);
 
-// Recovered weights of the first min(ceil(n/32), chunks) outlier chunks,
-// chunk-major [chunk][N][32] 16-bit (n read on the device).
 // Whether the weight-streaming GEMM kernel takes a shape (K % 16 == 0): it
 // reads each weight row once but every workgroup reads all of CA, so it
 // wins only on layers of at most 4096 outputs, for up to 32 tokens at any
@@ -61,6 +59,8 @@ hipError_t launch_recover_weight(int dt, const int8_t* CB, const float* SCB, int
 
 hipError_t launch_quant_vectorwise(int dt, const void* X, int64_t R, int64_t C, int zeropoint, int axis,
                                    int8_t* codes, float* scale, int32_t* zp, hipStream_t s);
+// Recovered weights of the first min(ceil(n/32), chunks) outlier chunks,
+// chunk-major [chunk][N][32] 16-bit (n read on the device).
 hipError_t launch_recover_outliers(int dt, const int8_t* CB, const float* SCB, int64_t N, int64_t K,
                                    const int32_t* idx, const int32_t* n_idx, void* wo, int chunks, hipStream_t s);
 

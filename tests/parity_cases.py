@@ -99,6 +99,27 @@ def _bits(x, dtype):
     return O.round_to_dtype_bits(x, "bf16").astype(np.uint16)
 
 
+SCATTERED = [(4096, 4096, 256), (300, 1024, 64), (100, 512, 64), (24, 256, 40)]
+
+
+def scattered_flags_case(T, K, N, dtype):
+    """Outlier values in single rows only, so that the bits of one bitmap
+    word come from many workgroups of 16 rows spread over the chip: column j
+    of the first 32 (and column 64 + 3 j of the next 96) exceeds the
+    threshold in one row of workgroup 8 j + j % 8 (taken modulo the
+    workgroups there are), and nowhere else."""
+    case = random_case(T, K, N, dtype=dtype, seed=T + 5 * K + N, n_out=0)
+    x = O.decode_bits(case.X, dtype).astype(np.float64)
+    groups = (T + 15) // 16
+    for j in range(32):
+        g = (8 * j + j % 8) % groups
+        for c in (j, 64 + 3 * j):
+            if c < K:
+                x[min(T - 1, 16 * g + j % 16), c] = 7.0 + j
+    case.X = _bits(x, dtype)
+    return case
+
+
 SMALL_T = [(1, 64, 64), (3, 48, 5), (16, 4096, 130), (8, 8192, 40), (16, 8448, 33), (5, 1024, 4097),
            (16, 256, 16), (2, 512, 3000), (11, 2048, 1000), (16, 64, 8192)]
 
@@ -295,6 +316,10 @@ def output_checks():
         for dt in ("f16", "bf16"):
             out.append((f"wide_ratio{T}x{K}x{N}-{dt}", lambda T=T, K=K, N=N, dt=dt: _own(wide_ratio_case(T, K, N, dt)),
                         None, None))
+    for T, K, N in SCATTERED:
+        for dt in ("f16", "bf16"):
+            out.append((f"scattered{T}x{K}x{N}-{dt}", lambda T=T, K=K, N=N, dt=dt:
+                        _own(scattered_flags_case(T, K, N, dt)), None, None))
     for T, K, N in MAX_K_SHAPES:
         out.append((f"maxk{T}x{K}x{N}", lambda T=T, K=K, N=N: _own(max_k_case(T, K, N)), None, None))
     out.append(("large_k_tiles", lambda: _own(large_k_tiles_case(), bias=False), LARGE_K_ROWS, LARGE_K_COLS))

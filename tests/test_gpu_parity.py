@@ -126,6 +126,17 @@ def test_activation_split_entry_point():
     assert np.array_equal(bitmap.cpu().numpy().view(np.uint32), O.outlier_bitmap(ridx, case.K))
 
 
+@pytest.mark.parametrize("T,K,N", PC.SCATTERED)
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+def test_scattered_outlier_flags_merge_across_the_chip(T, K, N, dtype):
+    """Each outlier value in a single row, so that the bits of one bitmap
+    word are set by workgroups on every compute die (the column scan ORs them
+    into the bitmap with atomics): the bitmap, list, codes and output are the
+    oracle's."""
+    g, r = _check_full(PC.scattered_flags_case(T, K, N, dtype))
+    assert g["n"] == min(K, 32) + len([j for j in range(32) if 64 + 3 * j < K])
+
+
 @pytest.mark.parametrize("T,K,N,coop", PC.WIDE_RATIO)
 @pytest.mark.parametrize("dtype", ["f16", "bf16"])
 def test_outlier_far_beyond_16_bits_leaves_its_neighbour(T, K, N, coop, dtype, monkeypatch):
@@ -339,7 +350,7 @@ def test_recovered_weights_bit_exact(dtype, every_column):
     assert n == K if every_column else n >= 40
     idx = ws.idx[:n].cpu().numpy()
     chunks = (n + 31) // 32
-    xb = T * ((K + 31) // 32 * 32) * 2
+    xb = B.lli8_scratch_bytes(T, K)  # the recovered weights follow the minimum scratch
     wo = ws.scratch[xb:xb + chunks * N * 64].cpu().numpy().view(np.uint16).reshape(chunks, N, 32)
     got = O.decode_bits(wo.transpose(1, 0, 2).reshape(N, chunks * 32), dtype).astype(np.float64)
     ref = O.recover_weight(CB.cpu().numpy()[:, idx], SCB.cpu().numpy(), dtype)
