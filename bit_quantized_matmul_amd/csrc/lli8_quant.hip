@@ -306,22 +306,47 @@ __global__ __launch_bounds__(256) void quant_rows_reg_kernel(
   const uint32_t* words = lds;
   const uint32_t* prefix = lds + W;
   if (row >= R) return;
-  uint32_t ob[MAXC];  // outlier columns of each chunk (bit e); chunks past the row end count as all-outlier
+  // Outlier columns (and chunks past the row end) are zeroed in place, so
+  // that neither the row maximum nor the codes need a mask per value: a zero
+  // value codes to 0.  Only chunk positions where some lane of the wave has
+  // such a column take the branch (outlier columns are few), and the outlier
+  // values go to Xo first.
 #pragma unroll
   for (int i = 0; i < MAXC; ++i) {
     const int64_t c = lane + (int64_t)i * WAVE;
-    uint32_t o = 0u;
-    if constexpr (EXCL) o = (words[c < nch ? (c >> 2) : 0] >> ((c & 3) * 8)) & 0xFFu;
-    ob[i] = (c < nch) ? o : 0xFFu;
+    uint32_t f = 0xFFu;
+    if (c < nch) f = EXCL ? (words[c >> 2] >> ((c & 3) * 8)) & 0xFFu : 0u;
+    if (__ballot(f != 0u) != 0) {
+      if constexpr (EXCL) {
+        // this chunk's outlier columns into Xo, a loop over the set bits (an
+        // unrolled test per column would keep a mask per column live)
+        uint32_t g = (c < nch && xo != nullptr) ? f : 0u;
+        if (g != 0u) {
+          const int64_t cw = c >> 2;
+          const uint32_t word = words[cw];
+          const int base = (int)prefix[cw];
+          while (g) {
+            const int e = __builtin_ctz(g);
+            g &= g - 1u;
+            const int bit = (int)((c & 3) * 8 + e);
+            const int p = base + __popc(word & ((1u << bit) - 1u));
+            xo[xo_offset(p, row, R)] = (uint16_t)half_bits(v[i], e);
+          }
+        }
+      }
+#pragma unroll
+      for (int d = 0; d < 4; ++d) {
+        // 0xFFFF in each half whose value is kept: (1 - flag) per half, times 0xFFFF
+        const uint32_t t = (((f >> (2 * d)) & 1u) | (((f >> (2 * d + 1)) & 1u) << 16)) ^ 0x00010001u;
+        v[i][d] &= t * 0xFFFFu;
+      }
+    }
   }
   uint32_t mx = 0u;
 #pragma unroll
   for (int i = 0; i < MAXC; ++i)
 #pragma unroll
-    for (int d = 0; d < 4; ++d) {
-      const uint32_t keep = (((ob[i] >> (2 * d)) & 1u) ? 0u : 0x7FFFu) | (((ob[i] >> (2 * d + 1)) & 1u) ? 0u : 0x7FFF0000u);
-      mx = pk_max_u16(mx, v[i][d] & keep);
-    }
+    for (int d = 0; d < 4; ++d) mx = pk_max_u16(mx, v[i][d] & 0x7FFF7FFFu);
   mx = max(mx & 0xFFFFu, mx >> 16);
 #pragma unroll
   for (int off = 32; off >= 1; off >>= 1) mx = max(mx, (uint32_t)__shfl_xor((int)mx, off, WAVE));
@@ -332,27 +357,9 @@ __global__ __launch_bounds__(256) void quant_rows_reg_kernel(
   for (int i = 0; i < MAXC; ++i) {
     const int64_t c = lane + (int64_t)i * WAVE;
     u32x2 pk;
-    pk[0] = pack_codes16(code_pair16<DT>(v[i][0], s), code_pair16<DT>(v[i][1], s)) & ~byte_mask4(ob[i]);
-    pk[1] = pack_codes16(code_pair16<DT>(v[i][2], s), code_pair16<DT>(v[i][3], s)) & ~byte_mask4(ob[i] >> 4);
+    pk[0] = pack_codes16(code_pair16<DT>(v[i][0], s), code_pair16<DT>(v[i][1], s));
+    pk[1] = pack_codes16(code_pair16<DT>(v[i][2], s), code_pair16<DT>(v[i][3], s));
     if (c < nch) cp[c] = pk;
-    if constexpr (EXCL) {
-      // this chunk's outlier columns into Xo: a branch the whole wave takes
-      // or skips, then a loop over the set bits (an unrolled test per column
-      // would keep a mask per column live and spill them)
-      uint32_t f = (c < nch && xo != nullptr) ? ob[i] : 0u;
-      if (__ballot(f != 0u) != 0) {
-        const int64_t cw = (c < nch ? c : 0) >> 2;
-        const uint32_t word = words[cw];
-        const int base = (int)prefix[cw];
-        while (f) {
-          const int e = __builtin_ctz(f);
-          f &= f - 1u;
-          const int bit = (int)((c & 3) * 8 + e);
-          const int p = base + __popc(word & ((1u << bit) - 1u));
-          xo[xo_offset(p, row, R)] = (uint16_t)half_bits(v[i], e);
-        }
-      }
-    }
   }
   if (lane == 0) scales[row] = m;
   if constexpr (EXCL) {
