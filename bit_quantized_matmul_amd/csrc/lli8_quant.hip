@@ -8,6 +8,8 @@
 // LLM.int8()" (steps 1-2) and "Quantization mechanics" (absmax bullet).
 // All three are HBM-bound streaming kernels: one wave owns a contiguous
 // stretch of a row and reads it with 16-byte loads.
+#include <algorithm>
+
 #include "lli8_device.h"
 #include "lli8_internal.h"
 
@@ -27,43 +29,11 @@ hipError_t launch_fill_u32(uint32_t* p, int64_t n, uint32_t v, hipStream_t s) {
 }
 
 // --------------------------------------------------------- outlier scan ----
-// Column c is an outlier when some row has |X[t, c]| > tau.  Lane owns one
+// Column c is an outlier when some row has |X[t, c]| > tau.  A lane owns one
 // 16-byte chunk (8 columns) and walks rows keeping packed 16-bit maxima of
 // the 15-bit magnitudes (one max per two values per row); the threshold test
-// is done once at the end on the raw bits.  Four lanes make one bitmap word,
-// which is OR-ed into the global bitmap only when non-zero (outlier columns
-// are rare, so atomics are rare).  Requires K % 8 == 0.
-template <int DT>
-__global__ __launch_bounds__(256) void scan_outliers_vec_kernel(
-    const uint16_t* __restrict__ X, int64_t T, int64_t K, float tau,
-    uint32_t* __restrict__ bitmap, int rows_per_block) {
-  constexpr int RPT = 8;  // rows per thread, loaded together
-  const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
-  const int64_t nch = K >> 3;
-  const int64_t c = (int64_t)blockIdx.x * 64 + lane;
-  const int64_t cc = c < nch ? c : nch - 1;
-  const u32x4* p = reinterpret_cast<const u32x4*>(X) + cc;
-  uint32_t m[4] = {0u, 0u, 0u, 0u};
-  for (int64_t rb = (int64_t)blockIdx.y * rows_per_block; rb < min(T, (int64_t)(blockIdx.y + 1) * rows_per_block);
-       rb += 4 * RPT) {
-    // rows past the end repeat the last row: a repeated row changes no maximum
-    u32x4 v[RPT];
-#pragma unroll
-    for (int i = 0; i < RPT; ++i) {
-      const int64_t r = rb + wid + 4 * i;
-      v[i] = p[(r < T ? r : T - 1) * nch];  // cached: the quantiser reads X again
-    }
-#pragma unroll
-    for (int i = 0; i < RPT; ++i)
-#pragma unroll
-      for (int d = 0; d < 4; ++d) m[d] = pk_max_u16(m[d], v[i][d] & 0x7FFF7FFFu);
-  }
-  const uint32_t flags = (c < nch) ? flags8(m, magnitude_threshold<DT>(tau)) : 0u;
-  uint32_t w = flags << ((lane & 3) * 8);
-  w |= __shfl_xor(w, 1, WAVE);
-  w |= __shfl_xor(w, 2, WAVE);
-  if ((lane & 3) == 0 && c < nch && w != 0u) atomicOr(bitmap + (c >> 2), w);
-}
+// is done once at the end on the raw bits.  Four lanes make one bitmap word.
+// K % 8 == 0: the strip kernels below; any K: one thread per column.
 
 // Any K: one thread per column, 64 columns per wave form two bitmap words.
 template <int DT>
@@ -134,6 +104,55 @@ __global__ __launch_bounds__(1024) void scan_outliers_full_kernel(
   }
 }
 
+// Many rows (K % 8 == 0): the 1024-thread strip workgroup above over a range
+// of rows, its final words ORed into the bitmap (non-zero ones only).  A grid
+// of about one workgroup per compute unit keeps the atomics few (1024
+// single-pass workgroups of four waves took 12.4 against 10.0 us at 4096 x
+// 4096 fp16), and sixteen waves of eight rows each keep 128 KiB of loads in
+// flight per compute unit: 4096 x 4096 fp16 7.85 us, 4096 x 12288 18.7 us,
+// against 8.2 and 20.1 us with four waves per workgroup.
+template <int DT>
+__global__ __launch_bounds__(1024) void scan_outliers_wide_kernel(
+    const uint16_t* __restrict__ X, int64_t T, int64_t K, float tau, uint32_t* __restrict__ bitmap,
+    int rows_per_block) {
+  constexpr int RPT = 8;  // rows per batch of loads
+  __shared__ uint32_t s_m[16][4][64];
+  const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+  const int64_t nch = K >> 3;
+  const int64_t c = (int64_t)blockIdx.x * 64 + lane;
+  const u32x4* p = reinterpret_cast<const u32x4*>(X) + (c < nch ? c : nch - 1);
+  const int64_t r_begin = (int64_t)blockIdx.y * rows_per_block;
+  const int64_t r_end = min(T, r_begin + rows_per_block);
+  uint32_t m[4] = {0u, 0u, 0u, 0u};
+  for (int64_t r0 = r_begin + wid; r0 < r_end; r0 += 16 * RPT) {
+    // rows past the range repeat its last row: a repeated row changes no maximum
+    u32x4 v[RPT];
+#pragma unroll
+    for (int i = 0; i < RPT; ++i) {
+      const int64_t r = r0 + 16 * i;
+      v[i] = p[(r < r_end ? r : r_end - 1) * nch];
+    }
+#pragma unroll
+    for (int i = 0; i < RPT; ++i)
+#pragma unroll
+      for (int d = 0; d < 4; ++d) m[d] = pk_max_u16(m[d], v[i][d] & 0x7FFF7FFFu);
+  }
+#pragma unroll
+  for (int d = 0; d < 4; ++d) s_m[wid][d][lane] = m[d];
+  __syncthreads();
+  if (wid == 0) {
+#pragma unroll
+    for (int d = 0; d < 4; ++d)
+#pragma unroll
+      for (int w = 1; w < 16; ++w) m[d] = pk_max_u16(m[d], s_m[w][d][lane]);
+    const uint32_t flags = (c < nch) ? flags8(m, magnitude_threshold<DT>(tau)) : 0u;
+    uint32_t word = flags << ((lane & 3) * 8);
+    word |= __shfl_xor(word, 1, WAVE);
+    word |= __shfl_xor(word, 2, WAVE);
+    if ((lane & 3) == 0 && c < nch && word != 0u) atomicOr(bitmap + (c >> 2), word);
+  }
+}
+
 bool scan_writes_all_words(int64_t T, int64_t K) { return T >= 1 && T <= SCAN_FULL_MAX_T && (K & 7) == 0; }
 
 hipError_t launch_scan_outliers(int dt, const void* X, int64_t T, int64_t K, float tau,
@@ -150,17 +169,16 @@ hipError_t launch_scan_outliers(int dt, const void* X, int64_t T, int64_t K, flo
   }
   if ((K & 7) == 0) {
     const int64_t gx = (K / 8 + 63) / 64;
-    // 32 rows per pass of a workgroup (4 waves x 8 rows); passes per
-    // workgroup grow until the grid is about 256 workgroups (4096 x 4096
-    // fp16: 10.0 us against 12.4 us with 1024 single-pass workgroups).
-    int rows = 32;
-    while (gx * ((T + 2 * rows - 1) / (2 * rows)) >= 256 && rows < 1024) rows *= 2;
+    // rows per workgroup: at least one batch of 128 (16 waves x 8 rows),
+    // else as many as make about one workgroup per compute unit
+    const int64_t gy_want = std::max<int64_t>(1, 256 / gx);
+    const int64_t rows = std::max<int64_t>(128, (T + gy_want - 1) / gy_want);
     const int64_t gy = (T + rows - 1) / rows;
     dim3 grid((unsigned)gx, (unsigned)gy);
     if (dt == DT_F16)
-      scan_outliers_vec_kernel<DT_F16><<<grid, 256, 0, s>>>(x, T, K, tau, bitmap, rows);
+      scan_outliers_wide_kernel<DT_F16><<<grid, 1024, 0, s>>>(x, T, K, tau, bitmap, (int)rows);
     else
-      scan_outliers_vec_kernel<DT_BF16><<<grid, 256, 0, s>>>(x, T, K, tau, bitmap, rows);
+      scan_outliers_wide_kernel<DT_BF16><<<grid, 1024, 0, s>>>(x, T, K, tau, bitmap, (int)rows);
   } else {
     const int64_t gx = (K + 255) / 256;
     const int rows = 64;
