@@ -29,6 +29,11 @@ The same number of steps then runs again in up to 10 blocks with one event
 pair each; "dispersion" gives the 10th, 50th and 90th percentiles of the
 blocks' per-step times.
 
+"achievable" holds two measured ceilings beside the nominal peaks: the rate
+of a loop of int8 matrix-core instructions on register operands and the
+bytes per second of a plain 1 GiB device copy; each roofline's
+"frac_of_achievable" divides its achieved rate by the ceiling of its unit.
+
 Prints one JSON line on stdout.  `value` is the effective throughput
 2*T*N*K / t in TOPS.  `roofline` describes the kernel with the largest average
 duration: for a one-kernel step that is the step time above; otherwise a
@@ -139,6 +144,56 @@ def measured_traffic(workload, kernel):
         if hashlib.sha256(f.read()).hexdigest() != rec["source_sha256"]:
             return None
     return int(rec["bytes_per_launch"])
+
+
+def achievable_peaks():
+    """Measured ceilings beside the nominal peaks: the int8 matrix cores in a
+    loop on register operands (no memory traffic; run long enough for the
+    board's clock under sustained matrix load to settle) and a plain 1 GiB
+    device-to-device copy (bytes read plus bytes written per second)."""
+    import torch
+    import bit_quantized_matmul_amd as B
+    iters = 4096  # about a millisecond per launch
+    sink, ops = B.lli8_mfma_i8_loop(iters)
+    torch.cuda.synchronize()
+    expect = ((4096 * iters + 2 ** 31) % 2 ** 32) - 2 ** 31
+    if int(sink[0].item()) != expect or int(sink[-1].item()) != expect:
+        raise RuntimeError("int8 matrix-core loop returned a wrong sum")
+    for _ in range(100):
+        B.lli8_mfma_i8_loop(iters, sink)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(20):
+        B.lli8_mfma_i8_loop(iters, sink)
+    e1.record()
+    torch.cuda.synchronize()
+    mfma_tops = ops * 20 / (e0.elapsed_time(e1) * 1e-3) / 1e12
+    n = 1 << 30
+    src = torch.empty(n, dtype=torch.uint8, device="cuda").fill_(1)
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    e0.record()
+    for _ in range(10):
+        dst.copy_(src)
+    e1.record()
+    torch.cuda.synchronize()
+    copy_gbs = 2.0 * n * 10 / (e0.elapsed_time(e1) * 1e-3) / 1e9
+    del src, dst
+    torch.cuda.empty_cache()
+    return {"mfma_i8_loop_tops": round(mfma_tops, 1), "mfma_i8_loop_frac": round(mfma_tops / INT8_PEAK_TOPS, 4),
+            "hbm_copy_gbs": round(copy_gbs, 1), "hbm_copy_frac": round(copy_gbs / HBM_PEAK_GBS, 4)}
+
+
+def frac_of_achievable(roof, ach):
+    """A roofline's achieved rate against the measured ceiling of its unit (int8 and HBM only)."""
+    if ach is None:
+        return None
+    if roof["bound"] == "mfma" and roof["peak"] == INT8_PEAK_TOPS:
+        return round(roof["achieved"] / ach["mfma_i8_loop_tops"], 4)
+    if roof["bound"] == "hbm":
+        return round(roof["achieved"] / ach["hbm_copy_gbs"], 4)
+    return None
 
 
 def copy_calibration(mib):
@@ -475,14 +530,17 @@ def main():
         if w not in CONFIGS:
             sys.exit(f"unknown workload {w!r}; choose from {sorted(CONFIGS)}")
     torch.cuda.set_device(torch.device("cuda:0"))
+    ach = achievable_peaks()
     case = config_case(args.workload)
     line = measure(args.workload, case, args)
+    line["roofline"]["frac_of_achievable"] = frac_of_achievable(line["roofline"], ach)
     print(f"[bench] {args.workload}: {line['ms_per_step']} ms per step, {line['value']} TOPS", file=sys.stderr,
           flush=True)
     extra = {}
     for w in names[1:]:
         torch.cuda.empty_cache()
         sub = measure(w, config_case(w), args)
+        sub["roofline"]["frac_of_achievable"] = frac_of_achievable(sub["roofline"], ach)
         print(f"[bench] {w}: {sub['ms_per_step']} ms per step, {sub['value']} TOPS", file=sys.stderr, flush=True)
         c = sub["config"]
         extra[w] = {"value": sub["value"], "unit": sub["unit"], "ms_per_step": sub["ms_per_step"],
@@ -491,6 +549,7 @@ def main():
                     "roofline": sub["roofline"], "dispersion": sub["dispersion"]}
     if extra:
         line["workloads"] = extra
+    line["achievable"] = ach
     torch.cuda.empty_cache()
     if not args.no_cpu_baseline:
         import oracle as O

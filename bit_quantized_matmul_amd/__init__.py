@@ -16,12 +16,13 @@ from ._lib import (LLI8_BF16, LLI8_F16, Lli8Error, Workspace, lib,  # noqa: F401
                    library_path, lli8_int8_linear, lli8_quant_rowwise_outliers, lli8_quant_vectorwise,
                    lli8_quant_weight_rowwise, lli8_recover_weight, lli8_scratch_bytes, lli8_scratch_bytes_full,
                    lli8_status_string, lli8_trace_enable, lli8_trace_read, lli8_version, lli8_workspace_bytes,
-                   lli8_int8_linear_noalloc, lli8_noalloc_scratch_bytes)
+                   lli8_int8_linear_noalloc, lli8_noalloc_scratch_bytes, lli8_mfma_i8_loop,
+                   lli8_mfma_i8_loop_sink_ints)
 
 __all__ = [
     "LLI8_F16", "LLI8_BF16", "Lli8Error", "Workspace", "lib", "library_path",
     "lli8_int8_linear", "lli8_quant_rowwise_outliers", "lli8_quant_vectorwise", "lli8_quant_weight_rowwise",
     "lli8_recover_weight", "lli8_workspace_bytes", "lli8_int8_linear_noalloc", "lli8_noalloc_scratch_bytes",
     "lli8_scratch_bytes", "lli8_scratch_bytes_full", "lli8_status_string", "lli8_trace_enable", "lli8_trace_read",
-    "lli8_version",
+    "lli8_version", "lli8_mfma_i8_loop", "lli8_mfma_i8_loop_sink_ints",
 ]

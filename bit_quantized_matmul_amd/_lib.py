@@ -97,6 +97,10 @@ def lib() -> ctypes.CDLL:
     L.lli8_last_error.restype = ctypes.c_char_p
     L.lli8_version.argtypes = []
     L.lli8_version.restype = ctypes.c_char_p
+    L.lli8_mfma_i8_loop.argtypes = [i64, vp, ctypes.POINTER(ctypes.c_double), vp]
+    L.lli8_mfma_i8_loop.restype = i32
+    L.lli8_mfma_i8_loop_sink_ints.argtypes = []
+    L.lli8_mfma_i8_loop_sink_ints.restype = ctypes.c_size_t
     L.lli8_trace_enable.argtypes = [i32]
     L.lli8_trace_enable.restype = None
     L.lli8_trace_read.argtypes = [ctypes.POINTER(_Trace)]
@@ -252,6 +256,28 @@ def lli8_recover_weight(CB, SCB, dtype=None, W=None, stream=None):
     _arg(W, "W", dev, dtype, N * K)
     _check(lib().lli8_recover_weight(_ptr(CB), _ptr(SCB), N, K, _dt(W), _ptr(W), _stream(dev, stream)))
     return W
+
+
+def lli8_mfma_i8_loop(iters: int, sink=None, device=None, stream=None):
+    """Calibration (not a step of the method): a loop of int8 matrix-core
+    instructions on register operands, one workgroup per compute unit.
+    Returns (sink, ops): sink int32 [lli8_mfma_i8_loop_sink_ints()], every
+    entry (4096 * iters) mod 2^32 once the launch is done; ops the int8
+    operations the launch performs."""
+    torch = _torch()
+    n = int(lib().lli8_mfma_i8_loop_sink_ints())
+    dev = _gpu(sink, "sink") if sink is not None else torch.device("cuda", torch.cuda.current_device()
+                                                                       if device is None else device)
+    if sink is None:
+        sink = torch.empty((n,), dtype=torch.int32, device=dev)
+    _arg(sink, "sink", dev, torch.int32, n)
+    ops = ctypes.c_double(0.0)
+    _check(lib().lli8_mfma_i8_loop(int(iters), _ptr(sink), ctypes.byref(ops), _stream(dev, stream)))
+    return sink, ops.value
+
+
+def lli8_mfma_i8_loop_sink_ints() -> int:
+    return int(lib().lli8_mfma_i8_loop_sink_ints())
 
 
 def lli8_workspace_bytes(T: int, K: int, N: int, dtype: int = LLI8_F16) -> int:

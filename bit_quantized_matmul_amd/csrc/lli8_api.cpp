@@ -277,6 +277,35 @@ lli8_status_t lli8_workspace_carve(void* base, size_t bytes, int64_t T, int64_t 
   return LLI8_OK;
 }
 
+// Compute units of the current device (calibration only; not cached).
+static int current_device_cus(hipError_t* err) {
+  int dev = 0, cus = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+  *err = e;
+  return e == hipSuccess ? cus : 0;
+}
+
+size_t lli8_mfma_i8_loop_sink_ints(void) {
+  hipError_t e;
+  const int cus = current_device_cus(&e);
+  return e == hipSuccess ? (size_t)cus * 512 : 0;
+}
+
+lli8_status_t lli8_mfma_i8_loop(int64_t iters, int32_t* sink, double* ops, void* stream) {
+  if (iters < 1) return fail(LLI8_ERR_SHAPE, "iters must be at least 1, got %lld", (long long)iters);
+  REQUIRE(sink, "sink");
+  if (ops == nullptr) return fail(LLI8_ERR_NULL, "ops is NULL");
+  hipError_t e;
+  const int cus = current_device_cus(&e);
+  if (e != hipSuccess) return hip_status(e, "device query");
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  TRY(hip_status(lli8::launch_mfma_i8_loop(iters, cus, sink, s), "mfma loop launch"));
+  // 8 waves x 8 instructions x 2 * 32^3 operations per iteration per workgroup
+  *ops = (double)cus * 8.0 * 8.0 * 65536.0 * (double)iters;
+  return LLI8_OK;
+}
+
 lli8_status_t lli8_recover_weight(const int8_t* CB, const float* SCB, int64_t N, int64_t K, lli8_dtype_t dtype,
                                   void* W, void* stream) {
   TRY(check_dtype(dtype));

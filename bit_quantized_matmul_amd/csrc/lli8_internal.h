@@ -53,6 +53,9 @@ inline bool stream_gemm_route(int64_t T, int64_t N, int64_t K) {
   return (K % 16) == 0 && N <= 4096 && (T <= 32 || (T <= 64 && K <= 4096));
 }
 
+// Calibration loop of int8 matrix-core instructions (lli8_calib.hip).
+hipError_t launch_mfma_i8_loop(int64_t iters, int blocks, int32_t* sink, hipStream_t s);
+
 // W = dtype(fl32(fl32(CB * SCB) / 127)) for a whole [N, K] weight.
 hipError_t launch_recover_weight(int dt, const int8_t* CB, const float* SCB, int64_t N, int64_t K, void* W,
                                  hipStream_t s);

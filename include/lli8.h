@@ -243,6 +243,24 @@ lli8_status_t lli8_quant_vectorwise(const void* X, int64_t R, int64_t C, lli8_dt
                                     float* scale, int32_t* zero_point, void* stream);
 
 /*
+ * Calibration, not a step of the method: how fast the int8 matrix cores run
+ * on this board with nothing else limiting them, for comparing the GEMM with
+ * an achievable peak beside the nominal one.  One 512-thread workgroup per
+ * compute unit; each of its eight waves issues 8 * iters
+ * v_mfma_i32_32x32x32_i8 on operands held in registers (every operand byte
+ * 1, so each thread's accumulators sum to 4096 * iters, modulo 2^32, which it
+ * writes to sink[thread]).
+ *   sink  device int32 buffer of lli8_mfma_i8_loop_sink_ints() entries
+ *         (512 per compute unit of the current device), 16-byte aligned
+ *   ops   host: receives the int8 operations the launch performs
+ *         (2 * 32^3 per instruction)
+ * Asynchronous on `stream`.  Errors: LLI8_ERR_SHAPE (iters < 1),
+ * LLI8_ERR_NULL, LLI8_ERR_ALIGN, LLI8_ERR_HIP.
+ */
+lli8_status_t lli8_mfma_i8_loop(int64_t iters, int32_t* sink, double* ops, void* stream);
+size_t lli8_mfma_i8_loop_sink_ints(void);
+
+/*
  * Optional kernel timing, for profiling.  While enabled (process-wide), each
  * kernel the entry points enqueue is bracketed by two HIP events recorded on
  * the call's stream.  lli8_trace_read waits for those events and reports the

@@ -160,6 +160,18 @@ def test_validation_recover_weight():
     assert f(None, None, 0, 8, 0, None, None) == 0                # nothing to do
 
 
+def test_validation_mfma_loop():
+    """The calibration loop refuses bad arguments before touching a device."""
+    import ctypes
+    L = _lib().lib()
+    ops = ctypes.c_double(0.0)
+    f = L.lli8_mfma_i8_loop
+    assert f(0, FAKE, ctypes.byref(ops), None) == 2           # iters < 1
+    assert f(8, None, ctypes.byref(ops), None) == 1           # sink NULL
+    assert f(8, FAKE + 4, ctypes.byref(ops), None) == 4       # sink misaligned
+    assert f(8, FAKE, None, None) == 1                        # ops NULL
+
+
 def test_workspace_bytes_and_carve():
     """One buffer split into the forward's buffers: every piece 256-byte
     aligned, in bounds, not overlapping, with room for 8 recovered-weight
