@@ -77,10 +77,9 @@ def zero_rows_case():
 # An outlier column beside a kept one, in rows whose kept values are tiny: the
 # outlier's value times the row's scale runs far past 16 bits (60 / 1e-3 x 127),
 # and the discarded code must not reach its neighbour.  One shape per route:
-# fused decode, one-launch split, strip scan, cooperative launch, separate
-# launches (cooperative launch off), any-K quantiser.
-WIDE_RATIO = [(8, 64, 40, "1"), (24, 64, 40, "1"), (100, 64, 40, "1"), (300, 64, 40, "1"), (300, 64, 40, "0"),
-              (300, 66, 40, "1")]
+# fused decode, one-launch split, strip scan over every row, scan over row
+# ranges, any-K quantiser.
+WIDE_RATIO = [(8, 64, 40), (24, 64, 40), (100, 64, 40), (300, 64, 40), (300, 66, 40)]
 
 
 def wide_ratio_case(T, K, N, dtype):
@@ -312,7 +311,7 @@ def output_checks():
             out.append((f"module-{dt}-{tau}", lambda dt=dt, tau=tau: (module_case(dt), tau), None, None))
     out += [("module_requant", lambda: (module_requant_case(), 6.0), None, None),
             ("module_reuse", lambda: (module_reuse_case(), 6.0), None, None)]
-    for T, K, N, _ in WIDE_RATIO:
+    for T, K, N in WIDE_RATIO:
         for dt in ("f16", "bf16"):
             out.append((f"wide_ratio{T}x{K}x{N}-{dt}", lambda T=T, K=K, N=N, dt=dt: _own(wide_ratio_case(T, K, N, dt)),
                         None, None))

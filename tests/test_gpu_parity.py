@@ -137,13 +137,12 @@ def test_scattered_outlier_flags_merge_across_the_chip(T, K, N, dtype):
     assert g["n"] == min(K, 32) + len([j for j in range(32) if 64 + 3 * j < K])
 
 
-@pytest.mark.parametrize("T,K,N,coop", PC.WIDE_RATIO)
+@pytest.mark.parametrize("T,K,N", PC.WIDE_RATIO)
 @pytest.mark.parametrize("dtype", ["f16", "bf16"])
-def test_outlier_far_beyond_16_bits_leaves_its_neighbour(T, K, N, coop, dtype, monkeypatch):
+def test_outlier_far_beyond_16_bits_leaves_its_neighbour(T, K, N, dtype):
     """An outlier value up to 4e6 times its row's scale (a row of tiny kept
     values) beside a kept column, on every activation route: the kept
     neighbour's code, and everything else, as the oracle's."""
-    monkeypatch.setenv("LLI8_COOP_ACT", coop)
     g, r = _check_full(PC.wide_ratio_case(T, K, N, dtype))
     assert g["n"] == 3
 
