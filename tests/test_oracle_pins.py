@@ -50,6 +50,24 @@ def test_absmax_worked_example_fp16():
     assert codes[0].tolist() == g["codes_derived"]
 
 
+def test_weight_bits_worked_example_and_row_selection():
+    """The weight quantiser on raw 16-bit patterns: the worked example's vector
+    as a weight row gives the page's codes and its fp16 absmax, and a row
+    subset gives exactly those rows of the whole weight's codes and scales."""
+    g = _load("absmax_worked_example.json")
+    W = np.stack([_f16([g["vector"]])[0], _f16([[-v for v in g["vector"]]])[0]])
+    CB, SCB = O.quantize_weight_bits(W, "f16")
+    assert CB[0].tolist() == g["codes_derived"]
+    assert CB[1].tolist() == [-c for c in g["codes_derived"]]
+    assert SCB.tolist() == [np.float32(5.3984375)] * 2
+    case = random_case(7, 40, 13, dtype="bf16", seed=5, n_out=0)
+    CBf, SCBf = O.quantize_weight_bits(case.W, "bf16")
+    assert np.isfinite(SCBf).all() and (SCBf > 0).all()
+    rows = [12, 0, 6]
+    CBr, SCBr = O.quantize_weight_bits(case.W, "bf16", rows=rows)
+    assert np.array_equal(CBr, CBf[rows]) and np.array_equal(SCBr, SCBf[rows])
+
+
 # ---------------------------------------------------------------- P-2 -----
 @pytest.mark.parametrize("dtype", ["f16", "bf16"])
 def test_weight_recovery_bound(dtype):
