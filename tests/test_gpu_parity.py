@@ -269,6 +269,38 @@ def test_graph_replays_match_eager(T, K, N):
         assert torch.equal(got_b, ref_b)
 
 
+def test_workspace_reused_across_outlier_paths():
+    """One workspace through calls whose outlier columns move between the
+    paths of the persistent kernel (five chunks staged through LDS, a few
+    taken from registers, every column an outlier, none at all) and back:
+    each call equals the oracle, so nothing an earlier call left in the
+    workspace (bitmap, list, count, recovered weights) reaches a later one."""
+    import torch
+    B = _lib()
+    T, K, N = 512, 256, 16384  # 128 whole 256 x 256 tiles: the persistent kernel
+    base = random_case(T, K, N, seed=801, n_out=0)
+    W = to_dev(base.W, "f16")
+    bias = to_dev(base.bias, "f16")
+    CB, SCB = B.lli8_quant_weight_rowwise(W)
+    CBr, SCBr = O.quantize_weight_bits(base.W, "f16")
+    assert np.array_equal(CB.cpu().numpy(), CBr)
+    ws = B.Workspace(T, K, N, torch.float16, "cuda", want_acc=True)
+    out = torch.empty((T, N), dtype=torch.float16, device="cuda")
+    for i, (n_out, tau) in enumerate([(150, 6.0), (3, 6.0), (0, 0.01), (2, 0.0), (100, 6.0), (150, 6.0)]):
+        case = random_case(T, K, N, seed=810 + i, n_out=n_out)
+        B.lli8_int8_linear(to_dev(case.X, "f16"), CB, SCB, bias, tau, out=out, ws=ws, want_acc=True)
+        torch.cuda.synchronize()
+        r = O.linear_forward(case.X, "f16", CBr, SCBr, base.bias, tau)
+        n = int(ws.n_idx.item())
+        assert n == r["idx"].size, (i, n_out, tau)
+        assert np.array_equal(ws.idx[:n].cpu().numpy(), r["idx"]), (i, n_out, tau)
+        assert np.array_equal(ws.bitmap.cpu().numpy().view(np.uint32), O.outlier_bitmap(r["idx"], K)), i
+        assert np.array_equal(ws.CA.cpu().numpy(), r["CA"]), i
+        assert np.array_equal(ws.SCA[:T].cpu().numpy(), r["SCA"]), i
+        assert np.array_equal(ws.acc.cpu().numpy(), r["acc"]), i
+        assert_out(bits_of(out), r, "f16", what=f"call {i} (n_out={n_out}, tau={tau})")
+
+
 @pytest.mark.parametrize("T,K,N,n_out,tau,dtype", PC.PERSISTENT)
 def test_persistent_tiles(T, K, N, n_out, tau, dtype):
     case = PC.persistent_case(T, K, N, n_out, tau, dtype)
