@@ -209,8 +209,8 @@ __global__ __launch_bounds__(FD_THREADS, 1) void decode_fused_kernel(
     const bool any = __ballot(lane < FD_CW && s_wany[lane & (FD_CW - 1)] != 0u) != 0;
     const uint32_t rmax2 = wave_max_by8_u16x2(s_wmax[lane >> 3][lane & 7]);
     const float sca_lo = to_f32<DT>(rmax2 & 0xFFFFu), sca_hi = to_f32<DT>(rmax2 >> 16);  // exact row absmax
-    const float sf_lo = (sca_lo > 0.0f) ? 127.0f / sca_lo : 0.0f;
-    const float sf_hi = (sca_hi > 0.0f) ? 127.0f / sca_hi : 0.0f;
+    const float sf_lo = row_factor(sca_lo);
+    const float sf_hi = row_factor(sca_hi);
     if (w == 0 && lane < 8) {
       s_sca[2 * lane] = sca_lo;
       s_sca[2 * lane + 1] = sca_hi;
@@ -226,8 +226,16 @@ __global__ __launch_bounds__(FD_THREADS, 1) void decode_fused_kernel(
             __builtin_bit_cast(int, (t & 1) ? sf_hi : sf_lo), t >> 1));
         const u32x4& v = xr[t];
         u32x2 cw;
-        cw[0] = pack_codes16(code_pair16<DT>(v[0], sf), code_pair16<DT>(v[1], sf)) & z0;
-        cw[1] = pack_codes16(code_pair16<DT>(v[2], sf), code_pair16<DT>(v[3], sf)) & z1;
+        const float am = __builtin_bit_cast(float, __builtin_amdgcn_readlane(
+            __builtin_bit_cast(int, (t & 1) ? sca_hi : sca_lo), t >> 1));
+        if (DT == DT_BF16 && tiny_absmax(am)) {  // uniform: row t's absmax
+          constexpr bool P = DT == DT_BF16;
+          cw[0] = pack_codes16(code_pair16<DT, P>(v[0], sf), code_pair16<DT, P>(v[1], sf)) & z0;
+          cw[1] = pack_codes16(code_pair16<DT, P>(v[2], sf), code_pair16<DT, P>(v[3], sf)) & z1;
+        } else {
+          cw[0] = pack_codes16(code_pair16<DT>(v[0], sf), code_pair16<DT>(v[1], sf)) & z0;
+          cw[1] = pack_codes16(code_pair16<DT>(v[2], sf), code_pair16<DT>(v[3], sf)) & z1;
+        }
         *reinterpret_cast<u32x2*>(&s_codes[code_off(t, c >> 1) + (c & 1) * 8]) = cw;
       }
     }

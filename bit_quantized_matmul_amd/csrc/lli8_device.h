@@ -72,10 +72,24 @@ __device__ __forceinline__ uint32_t half_bits(const u32x4& c, int e) {
   return (e & 1) ? (w >> 16) : (w & 0xFFFFu);
 }
 
+// A row whose absmax is below 2^-100 (only bf16 reaches it: the smallest fp16
+// absmax is 2^-24) has its values and its absmax scaled by 2^64 first, exactly,
+// so that 127 / absmax stays finite; wherever the plain factor is finite the
+// codes are the same either way.
+constexpr float TINY_ABSMAX = 0x1p-100f;
+constexpr float PRESCALE = 0x1p64f;
+__device__ __forceinline__ bool tiny_absmax(float m) { return m > 0.0f && m < TINY_ABSMAX; }
+// s = fl32(127 / absmax), with the absmax prescaled when it is tiny
+__device__ __forceinline__ float row_factor(float m) {
+  return (m > 0.0f) ? 127.0f / (tiny_absmax(m) ? m * PRESCALE : m) : 0.0f;
+}
+
 // The int8 code of x for a row whose scale factor is s = fl32(127 / absmax):
-// round(fl32(x * s)) with halves away from zero (roundf), kept in [-127, 127].
+// round(fl32(x * s)) with halves away from zero (roundf), kept in [-127, 127]
+// (PRE: x prescaled, for a row with a tiny absmax).
+template <bool PRE = false>
 __device__ __forceinline__ int quant_code(float x, float s) {
-  float v = x * s;
+  float v = (PRE ? x * PRESCALE : x) * s;
   float r = roundf(v);
   r = fminf(fmaxf(r, -127.0f), 127.0f);
   return (int)r;
@@ -99,18 +113,20 @@ __device__ __forceinline__ int cvt_rpi(float v) {
   return r;
 }
 
-template <int DT>
+template <int DT, bool PRE = false>
 __device__ __forceinline__ float scaled_abs(uint32_t bits16, float s) {
   if constexpr (DT == DT_F16)
     return __builtin_fmaf(__builtin_fabsf((float)__builtin_bit_cast(_Float16, (uint16_t)bits16)), s, 0.0f);
+  else if constexpr (PRE)
+    return (__uint_as_float((bits16 & 0x7FFFu) << 16) * PRESCALE) * s;
   else
     return __uint_as_float((bits16 & 0x7FFFu) << 16) * s;
 }
 
-template <int DT>
+template <int DT, bool PRE = false>
 __device__ __forceinline__ uint32_t code_pair16(uint32_t x, float s) {
-  const int mlo = cvt_rpi(scaled_abs<DT>(x & 0xFFFFu, s));
-  const int mhi = cvt_rpi(scaled_abs<DT>(x >> 16, s));
+  const int mlo = cvt_rpi(scaled_abs<DT, PRE>(x & 0xFFFFu, s));
+  const int mhi = cvt_rpi(scaled_abs<DT, PRE>(x >> 16, s));
   // the low 16 bits of each: a value of an excluded (outlier) column, scaled
   // by a row absmax taken without it, can run far past 16 bits, and its code
   // (discarded later) must not carry into its neighbour's half

@@ -9,6 +9,7 @@
 // All three are HBM-bound streaming kernels: one wave owns a contiguous
 // stretch of a row and reads it with 16-byte loads.
 #include <algorithm>
+#include <type_traits>
 
 #include "lli8_device.h"
 #include "lli8_internal.h"
@@ -369,16 +370,21 @@ __global__ __launch_bounds__(256) void quant_rows_reg_kernel(
 #pragma unroll
   for (int off = 32; off >= 1; off >>= 1) mx = max(mx, (uint32_t)__shfl_xor((int)mx, off, WAVE));
   const float m = to_f32<DT>(mx);  // exact absmax of the kept values
-  const float s = (m > 0.0f) ? 127.0f / m : 0.0f;
+  const float s = row_factor(m);
   u32x2* cp = reinterpret_cast<u32x2*>(codes + row * K);
+  auto put_codes = [&](auto PREc) {
+    constexpr bool PRE = decltype(PREc)::value;
 #pragma unroll
-  for (int i = 0; i < MAXC; ++i) {
-    const int64_t c = lane + (int64_t)i * WAVE;
-    u32x2 pk;
-    pk[0] = pack_codes16(code_pair16<DT>(v[i][0], s), code_pair16<DT>(v[i][1], s));
-    pk[1] = pack_codes16(code_pair16<DT>(v[i][2], s), code_pair16<DT>(v[i][3], s));
-    if (c < nch) cp[c] = pk;
-  }
+    for (int i = 0; i < MAXC; ++i) {
+      const int64_t c = lane + (int64_t)i * WAVE;
+      u32x2 pk;
+      pk[0] = pack_codes16(code_pair16<DT, PRE>(v[i][0], s), code_pair16<DT, PRE>(v[i][1], s));
+      pk[1] = pack_codes16(code_pair16<DT, PRE>(v[i][2], s), code_pair16<DT, PRE>(v[i][3], s));
+      if (c < nch) cp[c] = pk;
+    }
+  };
+  if (DT == DT_BF16 && tiny_absmax(m)) put_codes(std::integral_constant<bool, DT == DT_BF16>());  // uniform per row
+  else put_codes(std::false_type());
   if (lane == 0) scales[row] = m;
   if constexpr (EXCL) {
     if (xo != nullptr) xo_zero_pad(xo, total, row, R, lane);
@@ -410,14 +416,15 @@ __global__ __launch_bounds__(256) void quant_rows_any_kernel(
     if (!out) m = fmaxf(m, fabsf(to_f32<DT>(rp[k])));
   }
   m = wave_max(m);
-  const float s = (m > 0.0f) ? 127.0f / m : 0.0f;
+  const float s = row_factor(m);
+  const float pre = tiny_absmax(m) ? PRESCALE : 1.0f;  // (1: the plain product, unchanged)
   int8_t* cp = codes + row * K;
   for (int64_t k = lane; k < K; k += WAVE) {
     const uint32_t h = rp[k];
     bool out = false;
     if constexpr (EXCL) out = (words[k >> 5] >> (k & 31)) & 1u;
     int q = 0;
-    if (!out && m > 0.0f) q = quant_code(to_f32<DT>(h), s);
+    if (!out && m > 0.0f) q = quant_code(to_f32<DT>(h) * pre, s);
     cp[k] = (int8_t)q;
     if constexpr (EXCL) {
       if (out && xo != nullptr) {
@@ -541,11 +548,17 @@ __global__ __launch_bounds__(512) void split_small_kernel(
 #pragma unroll
   for (int i = 1; i < 8; ++i) bm = max(bm, s_max[i]);
   const float am = to_f32<DT>(bm);  // exact absmax of the row's kept values
-  const float sc = (am > 0.0f) ? 127.0f / am : 0.0f;
+  const float sc = row_factor(am);
   if (cok) {
     u32x2 pk;
-    pk[0] = pack_codes16(code_pair16<DT>(x[0], sc), code_pair16<DT>(x[1], sc)) & ~byte_mask4(ob);
-    pk[1] = pack_codes16(code_pair16<DT>(x[2], sc), code_pair16<DT>(x[3], sc)) & ~byte_mask4(ob >> 4);
+    if (DT == DT_BF16 && tiny_absmax(am)) {  // uniform: one row per workgroup
+      constexpr bool P = DT == DT_BF16;
+      pk[0] = pack_codes16(code_pair16<DT, P>(x[0], sc), code_pair16<DT, P>(x[1], sc)) & ~byte_mask4(ob);
+      pk[1] = pack_codes16(code_pair16<DT, P>(x[2], sc), code_pair16<DT, P>(x[3], sc)) & ~byte_mask4(ob >> 4);
+    } else {
+      pk[0] = pack_codes16(code_pair16<DT>(x[0], sc), code_pair16<DT>(x[1], sc)) & ~byte_mask4(ob);
+      pk[1] = pack_codes16(code_pair16<DT>(x[2], sc), code_pair16<DT>(x[3], sc)) & ~byte_mask4(ob >> 4);
+    }
     reinterpret_cast<u32x2*>(codes + row * K)[c] = pk;
   }
   if (xo != nullptr) {

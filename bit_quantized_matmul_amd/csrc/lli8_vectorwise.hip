@@ -5,7 +5,10 @@
 // lli8_quant.hip and lli8_decode.hip.
 //
 //   absmax:     code = clamp(round_half_away(fl32(x * fl32(127 / amax))), +-127),
-//               scale = amax (0 for an all-zero vector, codes 0)
+//               scale = amax (0 for an all-zero vector, codes 0); below 2^-100
+//               x and amax are scaled by 2^64 first, as in the forward
+//               (zero-point with a range below 254 / FLT_MAX is outside the
+//               contract: its stored factor nd would overflow)
 //   zero-point: lo = min(min x, 0), hi = max(max x, 0), nd = fl32(254 / fl32(hi - lo)),
 //               zp = round_half_away(fl32(-lo * nd)) - 127,
 //               code = clamp(round_half_away(fl32(x * nd)) + zp, +-127),
@@ -41,10 +44,13 @@ __device__ __forceinline__ void finish_stats(float lo, float hi, float& scale, i
       zp = 0;
     }
   } else {
+    // absmax: zp, unused by the scheme, carries the exponent by which the
+    // values are scaled first (64 for an absmax below 2^-100, where 127 /
+    // amax would overflow: the same prescaling as the forward's quantisers)
     const float amax = fmaxf(fabsf(lo), fabsf(hi));
     scale = amax;
-    mul = amax > 0.0f ? 127.0f / amax : 0.0f;
-    zp = 0;
+    mul = row_factor(amax);
+    zp = tiny_absmax(amax) ? 64 : 0;
   }
 }
 
@@ -52,7 +58,7 @@ __device__ __forceinline__ void finish_stats(float lo, float hi, float& scale, i
 template <int ZP>
 __device__ __forceinline__ int code_of(float x, float mul, int zp) {
   if (mul == 0.0f) return 0;
-  const int q = (int)roundf(x * mul) + (ZP ? zp : 0);
+  const int q = ZP ? (int)roundf(x * mul) + zp : (int)roundf(__builtin_ldexpf(x, zp) * mul);
   return q < -127 ? -127 : (q > 127 ? 127 : q);
 }
 

@@ -36,6 +36,9 @@
  *     row absmax itself; the dequantisation factor is SCA * SCB / 127^2.
  *   - Rounding of codes: round(fl32(x * fl32(127 / absmax))), halves away
  *     from zero.  A row whose absmax is 0 gets scale 0 and all-zero codes.
+ *     Below an absmax of 2^-100 (bf16 only), where 127 / absmax can
+ *     overflow fp32, x and the absmax are scaled by 2^64 first (exact); the
+ *     codes are the plain form's wherever that form is finite.
  *   - threshold: column c is an outlier when some |X[t, c]| > threshold
  *     (strict, compared in fp32).  threshold <= 0 or +inf: no outlier
  *     columns (plain vector-wise int8).  NaN: LLI8_ERR_THRESHOLD.
@@ -230,7 +233,10 @@ lli8_status_t lli8_recover_weight(const int8_t* CB, const float* SCB, int64_t N,
  *   zero_point = round_half_away(fl32(-lo * nd)) - 127 (the code of 0.0),
  *   code = clamp(round_half_away(fl32(x * nd)) + zero_point, -127, 127); an
  *   all-zero vector gets nd 0, zero point 0, codes 0.  x is recovered as
- *   (code - zero_point) / nd.
+ *   (code - zero_point) / nd.  A range narrower than 254 / FLT_MAX (bf16
+ *   only), whose nd would overflow, is outside the contract.
+ * Absmax codes of a vector with max |x| below 2^-100 are taken as in the
+ * forward (x and the absmax scaled by 2^64 first).
  * Inputs are finite.  Asynchronous on `stream`; pointers 16-byte aligned.
  * Errors: LLI8_ERR_NULL, _SHAPE (R or C negative), _DTYPE, _ALIGN, and
  * LLI8_ERR_UNSUPPORTED for an unknown scheme or axis, before anything is

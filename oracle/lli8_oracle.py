@@ -44,6 +44,10 @@ reason, in the design notes of the repository):
   * Whole outlier columns are excluded from the row absmax and set to 0 in CA.
   * Scale factor s = fl32(127 / absmax), code = round_half_away(fl32(x * s)),
     clamped to [-127, 127].  A row whose absmax is 0 gets SCA = 0 and CA = 0.
+    For an absmax below 2^-100 (bf16 only: an fp16 absmax is at least 2^-24)
+    127 / absmax can overflow float32; there x and the absmax are scaled by
+    2^64 first (exact), which gives the plain form's codes wherever that form
+    is finite.
   * SCA and SCB store the absmax itself, as float32.
   * The outlier product uses X unquantised and the recovered weight rounded to
     the activation dtype, in both weight modes.
@@ -76,6 +80,8 @@ import numpy as np
 F16 = "f16"
 BF16 = "bf16"
 INT8_MAX = 127
+TINY_ABSMAX = np.float32(2.0 ** -100)  # absmax below this: the row is scaled by PRESCALE first
+PRESCALE = np.float32(2.0 ** 64)
 
 
 # ---------------------------------------------------------------- dtypes ----
@@ -173,8 +179,13 @@ def absmax_quantize_rows(X: np.ndarray, excluded_cols=None):
     codes = np.zeros(Xr.shape, dtype=np.int8)
     live = amax > 0
     if np.any(live):
-        s = np.float32(INT8_MAX) / amax[live]            # fl32(127 / absmax)
-        v = Xr[live] * s[:, None]                          # fl32(x * s)
+        # Below 2^-100 (bf16 rows only) the absmax and the row are taken
+        # 2^64 larger first, exactly, so that 127 / absmax stays finite;
+        # wherever the plain factor is finite this changes no code.
+        a = amax[live]
+        pre = np.where(a < TINY_ABSMAX, PRESCALE, np.float32(1)).astype(np.float32)
+        s = np.float32(INT8_MAX) / (a * pre)               # fl32(127 / absmax)
+        v = (Xr[live] * pre[:, None]) * s[:, None]         # fl32(x * s)
         assert v.dtype == np.float32
         q = np.clip(round_half_away(v), -INT8_MAX, INT8_MAX)
         codes[live] = q.astype(np.int8)

@@ -3,7 +3,9 @@ half-integer: the cases where the rounding mode and the float32 product
 decide the code.  Rows are built on the CPU by brute force over fp16 values
 (row absmax m in [64, 128), x <= m), then quantised by every GPU path -- the
 single-launch decode kernel (T <= 16), the multi-kernel path and the weight
-quantiser -- and compared with the oracle bit for bit."""
+quantiser -- and compared with the oracle bit for bit.  Also bf16 rows whose
+absmax lies below 2^-100 (down to subnormals), where 127 / absmax would
+overflow float32, on every quantiser path."""
 import numpy as np
 import pytest
 
@@ -67,3 +69,74 @@ def test_tie_codes_weights():
     rCB, rSCB = O.quantize_weight(O.decode_bits(Wb, "f16"))
     assert np.array_equal(SCB.cpu().numpy(), rSCB)
     assert np.array_equal(CB.cpu().numpy(), rCB)
+
+
+# ------------------------------------------------ rows of tiny magnitude ----
+# bf16 rows whose absmax lies below 2^-100, where 127 / absmax can overflow
+# float32 (the quantisers then scale the row and its absmax by 2^64 first):
+# rows scaled by 2^-124 (absmax near 2^-122) and rows of subnormals, beside
+# ordinary rows, through every quantiser path.
+
+def _tiny_rows_bits(R, C, seed):
+    rng = np.random.default_rng(seed)
+    v = rng.standard_normal((R, C))
+    v[1::4] *= 2.0 ** -124
+    bits = O.round_to_dtype_bits(v, "bf16")
+    sub = rng.integers(1, 0x80, size=(R, C), dtype=np.uint16) | (rng.integers(0, 2, size=(R, C), dtype=np.uint16) << 15)
+    bits[3::4] = sub[3::4]
+    return bits
+
+
+@pytest.mark.parametrize("K", [520, 1001])
+def test_tiny_rows_weights(K):
+    import bit_quantized_matmul_amd as B
+    import torch
+    Wb = _tiny_rows_bits(64, K, seed=K)
+    CB, SCB = B.lli8_quant_weight_rowwise(to_dev(Wb, "bf16"))
+    torch.cuda.synchronize()
+    rCB, rSCB = O.quantize_weight(O.decode_bits(Wb, "bf16"))
+    assert (rSCB[1::4] < 2.0 ** -100).all() and (rSCB[3::4] < 2.0 ** -126).all()
+    assert np.array_equal(SCB.cpu().numpy(), rSCB)
+    assert np.array_equal(CB.cpu().numpy(), rCB)
+
+
+@pytest.mark.parametrize("fused", ["1", "0"])
+@pytest.mark.parametrize("T,K,tau", [(12, 512, 0.0), (12, 512, 6.0), (40, 1001, 6.0), (100, 520, 6.0), (300, 64, 2.5)])
+def test_tiny_rows_activations(T, K, tau, fused, monkeypatch):
+    """The fused decode (T <= 16), the one-launch split (T <= 32), the any-K
+    quantiser (K % 8 != 0) and the register quantiser, with and without
+    outlier columns; the output too."""
+    import bit_quantized_matmul_amd as B
+    import torch
+    from tests.gpu_helpers import assert_out, bits_of
+    monkeypatch.setenv("LLI8_FUSED_DECODE", fused)
+    Xb = _tiny_rows_bits(T, K, seed=T + K)
+    Xb[0, 7] = O.round_to_dtype_bits(np.array([9.5]), "bf16")[0]  # an outlier column from an ordinary row
+    X = O.decode_bits(Xb, "bf16")
+    Wb = _tiny_rows_bits(48, K, seed=7)
+    CB, SCB = B.lli8_quant_weight_rowwise(to_dev(Wb, "bf16"))
+    out, ws = B.lli8_int8_linear(to_dev(Xb, "bf16"), CB, SCB, None, tau, want_acc=True)
+    torch.cuda.synchronize()
+    rCB, rSCB = O.quantize_weight(O.decode_bits(Wb, "bf16"))
+    r = O.linear_forward(Xb, "bf16", rCB, rSCB, None, tau)
+    n = int(ws.n_idx.item())
+    assert np.array_equal(ws.idx[:n].cpu().numpy(), r["idx"])
+    assert (r["SCA"][1::4] < 2.0 ** -100).all()
+    assert np.array_equal(ws.SCA[:T].cpu().numpy(), r["SCA"])
+    assert np.array_equal(ws.CA.cpu().numpy(), r["CA"])
+    assert np.array_equal(ws.acc.cpu().numpy(), r["acc"])
+    assert_out(bits_of(out), r, "bf16")
+
+
+@pytest.mark.parametrize("axis", ["rows", "cols"])
+def test_tiny_vectors_vectorwise_absmax(axis):
+    import bit_quantized_matmul_amd as B
+    import torch
+    Xb = _tiny_rows_bits(64, 96, seed=3)
+    if axis == "cols":
+        Xb = np.ascontiguousarray(Xb.T)
+    codes, scale, _ = B.lli8_quant_vectorwise(to_dev(Xb, "bf16"), "absmax", axis)
+    torch.cuda.synchronize()
+    rc, rs = O.absmax_quantize(O.decode_bits(Xb, "bf16"), 1 if axis == "rows" else 0)
+    assert np.array_equal(scale.cpu().numpy(), rs)
+    assert np.array_equal(codes.cpu().numpy(), rc)

@@ -68,6 +68,45 @@ def test_weight_bits_worked_example_and_row_selection():
     assert np.array_equal(CBr, CBf[rows]) and np.array_equal(SCBr, SCBf[rows])
 
 
+@pytest.mark.parametrize("k", [90, 100, 118, 122, 124])
+def test_tiny_rows_keep_their_codes(k):
+    """Scaling a row by a power of two (exactly) leaves its codes unchanged and
+    scales its absmax, also where the absmax falls below 2^-100 and 127 /
+    absmax would overflow float32 (k >= 122 here): the quantiser scales such
+    a row and its absmax by 2^64 first.  bf16 rows with magnitudes in
+    [2^-4, 4], so 2^-k times them stays a normal (exact) bf16 value."""
+    rng = np.random.default_rng(k)
+    mag = np.exp2(rng.uniform(-4, 2, size=(6, 40)))
+    X = O.decode_bits(O.round_to_dtype_bits(mag * rng.choice([-1.0, 1.0], size=mag.shape), "bf16"), "bf16")
+    X[1, ::3] = 0.0                                    # zeros in a row
+    codes, amax = O.absmax_quantize_rows(X)
+    scaled = (X.astype(np.float64) * 2.0 ** -k).astype(np.float32)
+    assert np.array_equal(scaled.astype(np.float64) * 2.0 ** k, X.astype(np.float64))  # exact
+    codes2, amax2 = O.absmax_quantize_rows(scaled)
+    assert np.array_equal(codes2, codes)
+    assert np.array_equal(amax2.astype(np.float64), amax.astype(np.float64) * 2.0 ** -k)
+    assert (np.abs(codes).max(axis=1) == 127).all()
+
+
+def test_subnormal_rows_code_like_their_scaled_copies():
+    """Rows of bf16 subnormals (absmax down to 2^-133): their codes equal those
+    of the same rows scaled up by 2^64, which is exact and lands in the normal
+    range, and the row maximum gets code 127."""
+    rng = np.random.default_rng(5)
+    bits = rng.integers(1, 0x80, size=(5, 24), dtype=np.uint16)      # bf16 subnormals
+    bits |= (rng.integers(0, 2, size=bits.shape, dtype=np.uint16) << 15)  # either sign
+    bits[0] = 0x0001                                                  # every value the smallest subnormal
+    bits[1, 5:] = 0                                                   # zeros beside them
+    X = O.decode_bits(bits, "bf16")
+    assert (np.abs(X) < 2.0 ** -126).all()
+    codes, amax = O.absmax_quantize_rows(X)
+    big = (X.astype(np.float64) * 2.0 ** 64).astype(np.float32)
+    codes2, _ = O.absmax_quantize_rows(big)
+    assert np.array_equal(codes, codes2)
+    assert (np.abs(codes).max(axis=1) == 127).all()
+    assert np.array_equal(codes[0], np.where(X[0] > 0, 127, -127).astype(np.int8))
+
+
 # ---------------------------------------------------------------- P-2 -----
 @pytest.mark.parametrize("dtype", ["f16", "bf16"])
 def test_weight_recovery_bound(dtype):
