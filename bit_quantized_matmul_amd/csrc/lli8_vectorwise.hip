@@ -19,6 +19,8 @@
 // same row (in cache by then).  Column-wise: one workgroup per 32- or
 // 64-column strip walking every row twice (statistics, then codes), 8
 // columns per thread; one launch, no atomics, no scratch.
+#include <type_traits>
+
 #include "lli8_device.h"
 #include "lli8_internal.h"
 
@@ -54,11 +56,12 @@ __device__ __forceinline__ void finish_stats(float lo, float hi, float& scale, i
   }
 }
 
-// One code; mul = 0 marks an all-zero vector (code 0).
-template <int ZP>
+// One code; mul = 0 marks an all-zero vector (code 0).  PRE = false: the
+// caller knows the absmax prescale exponent zp is 0.
+template <int ZP, bool PRE = true>
 __device__ __forceinline__ int code_of(float x, float mul, int zp) {
   if (mul == 0.0f) return 0;
-  const int q = ZP ? (int)roundf(x * mul) + zp : (int)roundf(__builtin_ldexpf(x, zp) * mul);
+  const int q = ZP ? (int)roundf(x * mul) + zp : (int)roundf((PRE ? __builtin_ldexpf(x, zp) : x) * mul);
   return q < -127 ? -127 : (q > 127 ? 127 : q);
 }
 
@@ -119,18 +122,24 @@ __global__ __launch_bounds__(256) void vw_rows_kernel(const uint16_t* __restrict
     if (ZP) zpo[r] = zp;
   }
   int8_t* crow = codes + r * C;
-  if constexpr (VEC) {
-    const int64_t nch = C >> 3;
-    for (int64_t c = lane; c < nch; c += 64) {
-      const u32x4 v = *reinterpret_cast<const u32x4*>(row + 8 * c);
-      int q[8];
+  auto put = [&](auto PREc) {
+    constexpr bool PRE = decltype(PREc)::value;
+    if constexpr (VEC) {
+      const int64_t nch = C >> 3;
+      for (int64_t c = lane; c < nch; c += 64) {
+        const u32x4 v = *reinterpret_cast<const u32x4*>(row + 8 * c);
+        int q[8];
 #pragma unroll
-      for (int e = 0; e < 8; ++e) q[e] = code_of<ZP>(to_f32<DT>(half_bits(v, e)), mul, zp);
-      *reinterpret_cast<u32x2*>(crow + 8 * c) = (u32x2){pack4(q[0], q[1], q[2], q[3]), pack4(q[4], q[5], q[6], q[7])};
+        for (int e = 0; e < 8; ++e) q[e] = code_of<ZP, PRE>(to_f32<DT>(half_bits(v, e)), mul, zp);
+        *reinterpret_cast<u32x2*>(crow + 8 * c) = (u32x2){pack4(q[0], q[1], q[2], q[3]), pack4(q[4], q[5], q[6], q[7])};
+      }
+    } else {
+      for (int64_t c = lane; c < C; c += 64) crow[c] = (int8_t)code_of<ZP, PRE>(to_f32<DT>(row[c]), mul, zp);
     }
-  } else {
-    for (int64_t c = lane; c < C; c += 64) crow[c] = (int8_t)code_of<ZP>(to_f32<DT>(row[c]), mul, zp);
-  }
+  };
+  // (absmax: the prescale only for a row with a tiny absmax; uniform per row)
+  if (!ZP && zp != 0) put(std::true_type());
+  else put(std::false_type());
 }
 
 // --------------------------------------------------------- column-wise ----
