@@ -129,10 +129,13 @@ def test_tiny_rows_activations(T, K, tau, fused, monkeypatch):
 
 
 @pytest.mark.parametrize("axis", ["rows", "cols"])
-def test_tiny_vectors_vectorwise_absmax(axis):
+@pytest.mark.parametrize("n,length", [(64, 96), (24, 3000), (24, 5000)])
+def test_tiny_vectors_vectorwise_absmax(axis, n, length):
+    # n vectors of `length` values: rows held in registers (2, 8 or 24 chunks
+    # per lane), columns 8 or 32 rows per thread in registers, or walked twice
     import bit_quantized_matmul_amd as B
     import torch
-    Xb = _tiny_rows_bits(64, 96, seed=3)
+    Xb = _tiny_rows_bits(n, length, seed=3)
     if axis == "cols":
         Xb = np.ascontiguousarray(Xb.T)
     codes, scale, _ = B.lli8_quant_vectorwise(to_dev(Xb, "bf16"), "absmax", axis)

@@ -9,8 +9,13 @@ from workloads import matrix_bits
 
 pytestmark = pytest.mark.gpu
 
+# Routes: rows held in registers (C <= 1024, 4096, 12288) or walked twice
+# (C > 12288); a column strip's rows held in registers (8, 16 or 32 per
+# thread: R <= 1024, 2048, 4096 with 32-column strips, half that with the
+# 64-column strips of C >= 16384) or walked twice; C % 8 != 0 per value.
 SHAPES = [(37, 136), (64, 200), (33, 13), (1, 8), (5, 1), (513, 1000), (130, 64), (7, 4096), (300, 71),
-          (9, 16392), (5, 16390)]  # the last two: 64-column strips (C >= 16384)
+          (9, 16392), (5, 16390),  # 64-column strips (C >= 16384)
+          (40, 12000), (2000, 96), (4096, 40), (4100, 24), (700, 16384), (1100, 16384)]
 
 
 def _ref(bits, dtype, scheme, axis):
