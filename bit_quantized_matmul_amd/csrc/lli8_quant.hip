@@ -334,7 +334,7 @@ __global__ __launch_bounds__(256) void quant_rows_reg_kernel(
   // are followed by a wait for every memory operation in flight (loads and
   // stores share one counter), so every further chunk with an outlier column
   // waits for the previous one's stores to land (4096 x 4096 fp16, four
-  // outlier columns: 13.7 -> 11.9 us).
+  // outlier columns, back to back: 13.6 -> 13.1 us per launch).
   if constexpr (EXCL) __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
   // Outlier columns (and chunks past the row end) are zeroed in place, so
   // that neither the row maximum nor the codes need a mask per value: a zero
