@@ -2,8 +2,8 @@
 
 Every case patches one step of the oracle module, reruns the pin test that
 guards that step, and expects it to fail.  This shows the pins are not
-vacuous: a dropped term, a wrong comparison, rounding mode, scale or a
-transposed operand all break at least one of them.
+vacuous: a dropped term, a wrong comparison, rounding mode, scale, axis,
+order or sign, or a transposed operand all break at least one of them.
 """
 import numpy as np
 import pytest
@@ -54,8 +54,50 @@ def _scale_div_not_mul(X, excluded_cols=None):
     return codes, amax
 
 
+def _outliers_over_rows(X, threshold):
+    # the maximum taken along the wrong axis: flags rows, not feature columns
+    tau = np.float32(threshold)
+    if not tau > 0 or X.shape[0] == 0:
+        return np.zeros(0, np.int32)
+    return np.nonzero(np.max(np.abs(X), axis=1) > tau)[0].astype(np.int32)
+
+
+def _outliers_descending(X, threshold):
+    return _orig_outliers(X, threshold)[::-1].copy()
+
+
+def _outliers_signed(X, threshold):
+    # x > tau instead of |x| > tau: large negative values are missed
+    tau = np.float32(threshold)
+    if not tau > 0 or X.shape[0] == 0:
+        return np.zeros(0, np.int32)
+    return np.nonzero(np.max(X, axis=0) > tau)[0].astype(np.int32)
+
+
+def _weight_scale_per_input_feature(W):
+    # one scale per column of W [N, K] instead of per output row
+    codes, amax = _orig_absmax(np.asarray(W, np.float32).T, None)
+    return codes.T.copy(), amax
+
+
+def _signed_row_max(X, excluded_cols=None):
+    # max(x) instead of max(|x|): rows led by a negative value get clipped codes
+    X = np.array(X, np.float32, copy=True)
+    if excluded_cols is not None and len(excluded_cols):
+        X[:, np.asarray(excluded_cols)] = 0
+    amax = (np.max(X, axis=1) if X.shape[1] else np.zeros(X.shape[0], np.float32)).astype(np.float32)
+    amax = np.maximum(amax, np.float32(0))
+    codes = np.zeros(X.shape, np.int8)
+    live = amax > 0
+    if np.any(live):
+        v = X[live] * (np.float32(127) / amax[live])[:, None]
+        codes[live] = np.clip(M.round_half_away(v), -127, 127).astype(np.int8)
+    return codes, amax
+
+
 _orig_absmax = M.absmax_quantize_rows
 _orig_acc = M.int8_accumulate
+_orig_outliers = M.outlier_columns
 
 
 def _reload_pins(monkeypatch, name, fn):
@@ -74,6 +116,11 @@ MUTATIONS = [
     ("recover_weight", _recover_no_div, P.test_weight_recovery_bound, ("f16",)),
     ("int8_accumulate", _acc_transposed_weight, P.test_integer_special_case_is_textbook_matmul, ()),
     ("absmax_quantize_rows", _scale_div_not_mul, P.test_absmax_worked_example_fp32, ()),
+    ("outlier_columns", _outliers_over_rows, P.test_issue_tiny_threshold_flags_every_column, ()),
+    ("outlier_columns", _outliers_descending, P.test_tiny_config_outlier_columns, ()),
+    ("outlier_columns", _outliers_signed, P.test_threshold_is_strict, ()),
+    ("quantize_weight", _weight_scale_per_input_feature, P.test_weight_bits_worked_example_and_row_selection, ()),
+    ("absmax_quantize_rows", _signed_row_max, P.test_weight_bits_worked_example_and_row_selection, ()),
 ]
 
 
