@@ -1,7 +1,8 @@
 """Plant plausible mistakes in the oracle's zero-point quantiser (on the CPU)
 and check that one of its pins fails for each: a 255-wide scale, a zero point
 without the -127 shift, a range not widened to contain 0, half-to-even
-rounding."""
+rounding, the zero point added before the rounding, the zero point taken from
+the top of the range."""
 import numpy as np
 import pytest
 
@@ -39,6 +40,35 @@ def _half_even(v):
     return np.rint(np.asarray(v, np.float64))
 
 
+def _shifted_rounding(zp_from_top):
+    """The two remaining slips in the code and zero-point formulas: the zero
+    point added before the rounding (round(x * nd + zp)), or the zero point
+    taken from the top of the range (127 - round(hi * nd))."""
+    def q(X):
+        X = np.asarray(X, dtype=np.float32)
+        R, C = X.shape
+        if C == 0:
+            return np.zeros((R, 0), np.int8), np.zeros(R, np.float32), np.zeros(R, np.int32)
+        lo = np.minimum(X.min(axis=1), np.float32(0)).astype(np.float32)
+        hi = np.maximum(X.max(axis=1), np.float32(0)).astype(np.float32)
+        width = (hi - lo).astype(np.float32)
+        nd = np.zeros(R, np.float32)
+        zp = np.zeros(R, np.int32)
+        codes = np.zeros((R, C), np.int8)
+        live = width > 0
+        nd[live] = np.float32(254.0) / width[live]
+        v = (X[live] * nd[live][:, None]).astype(np.float32)
+        if zp_from_top:
+            zp[live] = (127 - M.round_half_away((hi[live] * nd[live]).astype(np.float32))).astype(np.int32)
+            q8 = M.round_half_away(v) + zp[live][:, None]
+        else:
+            zp[live] = (M.round_half_away((-lo[live] * nd[live]).astype(np.float32)) - 127).astype(np.int32)
+            q8 = M.round_half_away(v + zp[live][:, None].astype(np.float32))
+        codes[live] = np.clip(q8, -127, 127).astype(np.int8)
+        return codes, nd, zp
+    return q
+
+
 PINS = [P.test_zeropoint_range_endpoints_and_symmetric_case,
         lambda: [P.test_zeropoint_closed_forms(*c) for c in (
             ([0.0, 1.0, 2.0], 127.0, -127, [-127, 0, 127]),
@@ -50,8 +80,9 @@ PINS = [P.test_zeropoint_range_endpoints_and_symmetric_case,
 
 
 @pytest.mark.parametrize("mutant", [
-    _variant(scale=255.0), _variant(shift=0), _variant(widen=False), _variant(rnd=_half_even)],
-    ids=["scale-255", "no-shift", "range-not-widened", "half-even"])
+    _variant(scale=255.0), _variant(shift=0), _variant(widen=False), _variant(rnd=_half_even),
+    _shifted_rounding(False), _shifted_rounding(True)],
+    ids=["scale-255", "no-shift", "range-not-widened", "half-even", "zp-before-rounding", "zp-from-top"])
 def test_a_pin_catches(mutant, monkeypatch):
     monkeypatch.setattr(M, "zeropoint_quantize_rows", mutant)
     failed = 0
