@@ -146,18 +146,51 @@ __global__ __launch_bounds__(256) void vw_rows_kernel(const uint16_t* __restrict
   else put(std::false_type());
 }
 
-// Rows of at most 512 * MAXC values (C % 8 == 0): the row is held in
-// registers (MAXC 16-byte chunks per lane), so it is read from memory once
+// Zero-point statistics on raw 16-bit values: a key that orders fp16 and
+// bf16 bit patterns like the values they encode (a negative value has every
+// bit flipped, a positive one its sign bit set), two keys per dword.
+__device__ __forceinline__ uint32_t order_keys16(uint32_t w) {
+  const uint32_t neg = __builtin_bit_cast(uint32_t, __builtin_bit_cast(i16x2, w) >> 15);  // 0xFFFF where negative
+  return w ^ (neg | 0x80008000u);
+}
+__device__ __forceinline__ uint32_t key_bits16(uint32_t k) {  // inverse of one key
+  return (k & 0x8000u) ? (k & 0x7FFFu) : (~k & 0xFFFFu);
+}
+__device__ __forceinline__ uint32_t pk_min_u16(uint32_t a, uint32_t b) {
+  return __builtin_bit_cast(uint32_t, __builtin_elementwise_min(__builtin_bit_cast(u16x2, a), __builtin_bit_cast(u16x2, b)));
+}
+
+// Two zero-point codes clamp(round_half_away(fl32(x * nd)) + zp, +-127) as
+// int16 halves of one dword.  The magnitude is floor(|v| + 0.5) for
+// v = fl32(x * nd), |v| <= 254, by one conversion; mantissa bit 0 of |v| is
+// cleared first, after which the result is the same whether or not the
+// conversion rounds |v| + 0.5 to fp32 (no tie k + 0.5 below 2^22 has that
+// bit set, and the rounded sum is then exact).  zp2: the zero point in both
+// halves.
+template <int DT>
+__device__ __forceinline__ uint32_t zp_code_pair16(uint32_t x, float nd, uint32_t zp2) {
+  const int mlo = cvt_rpi(__uint_as_float(__float_as_uint(scaled_abs<DT>(x & 0xFFFFu, nd)) & ~1u));
+  const int mhi = cvt_rpi(__uint_as_float(__float_as_uint(scaled_abs<DT>(x >> 16, nd)) & ~1u));
+  const i16x2 mag = __builtin_bit_cast(i16x2, __builtin_amdgcn_perm((uint32_t)mhi, (uint32_t)mlo, 0x05040100u));
+  const i16x2 neg = __builtin_bit_cast(i16x2, x) >> 15;  // -1 where x < 0
+  const i16x2 q = ((mag ^ neg) - neg) + __builtin_bit_cast(i16x2, zp2);
+  const i16x2 lim = {127, 127};
+  return __builtin_bit_cast(uint32_t, __builtin_elementwise_max(__builtin_elementwise_min(q, lim), -lim));
+}
+
+// Zero-point, rows of at most 512 * MAXC values (C % 8 == 0): the row is held
+// in registers (MAXC 16-byte chunks per lane), so it is read from memory once
 // and every code store comes after the only wait.  (The two-pass kernel above
 // reloads a chunk after each store, and loads and stores share one
 // completion counter, so each reload also waits for the previous store:
-// 4096 x 4096 fp16, zero-point, 15.9 -> 14.5 us per kernel.)  Chunks past
-// the row end re-read chunk 0, which changes no minimum or maximum, and store
-// nothing.
-template <int DT, int ZP, int MAXC>
-__global__ __launch_bounds__(256) void vw_rows_reg_kernel(const uint16_t* __restrict__ X, int64_t R, int64_t C,
-                                                          int8_t* __restrict__ codes, float* __restrict__ scale,
-                                                          int32_t* __restrict__ zpo) {
+// 4096 x 4096 fp16 15.9 -> 14.5 us per kernel.)  The row's minimum and
+// maximum are taken on ordering keys, both in one packed wave reduction, and
+// the codes two at a time with packed 16-bit arithmetic.  Chunks past the row
+// end re-read chunk 0, which changes no minimum or maximum, and store nothing.
+template <int DT, int MAXC>
+__global__ __launch_bounds__(256) void vw_rows_zp_kernel(const uint16_t* __restrict__ X, int64_t R, int64_t C,
+                                                         int8_t* __restrict__ codes, float* __restrict__ scale,
+                                                         int32_t* __restrict__ zpo) {
   const int lane = threadIdx.x & 63;
   const int64_t r = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
   if (r >= R) return;
@@ -169,41 +202,42 @@ __global__ __launch_bounds__(256) void vw_rows_reg_kernel(const uint16_t* __rest
     const int64_t c = lane + (int64_t)i * 64;
     v[i] = rp[c < nch ? c : 0];
   }
-  float lo = 0.0f, hi = 0.0f;  // 0 is inside either scheme's range already
+  uint32_t kmin = 0xFFFFFFFFu, kmax = 0u;
 #pragma unroll
   for (int i = 0; i < MAXC; ++i)
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const float x = to_f32<DT>(half_bits(v[i], e));
-      lo = fminf(lo, x);
-      hi = fmaxf(hi, x);
+    for (int d = 0; d < 4; ++d) {
+      const uint32_t k = order_keys16(v[i][d]);
+      kmin = pk_min_u16(kmin, k);
+      kmax = pk_max_u16(kmax, k);
     }
-  lo = wave_min(lo);
-  hi = wave_max(hi);
+  // the largest key in the high half, the complement of the smallest in the
+  // low half: one packed maximum over the wave reduces both
+  uint32_t mm = (max(kmax & 0xFFFFu, kmax >> 16) << 16) | (0xFFFFu - min(kmin & 0xFFFFu, kmin >> 16));
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) mm = pk_max_u16(mm, (uint32_t)__shfl_xor((int)mm, off, WAVE));
+  const float lo = to_f32<DT>(key_bits16(0xFFFFu - (mm & 0xFFFFu)));
+  const float hi = to_f32<DT>(key_bits16(mm >> 16));
   float sc, mul;
   int zp;
-  finish_stats<ZP>(lo, hi, sc, zp, mul);
+  finish_stats<1>(lo, hi, sc, zp, mul);  // widens [lo, hi] to contain 0
   if (lane == 0) {
     scale[r] = sc;
-    if (ZP) zpo[r] = zp;
+    zpo[r] = zp;
   }
-  // the 16-bit row, not its fp32 conversion, stays live into the code pass
+  const uint32_t zp2 = ((uint32_t)zp & 0xFFFFu) | ((uint32_t)zp << 16);
+  // the 16-bit row, not fp32 conversions of it, stays live into the code pass
 #pragma unroll
   for (int i = 0; i < MAXC; ++i) asm volatile("" : "+v"(v[i]));
   u32x2* cp = reinterpret_cast<u32x2*>(codes + r * C);
-  auto put = [&](auto PREc) {
-    constexpr bool PRE = decltype(PREc)::value;
 #pragma unroll
-    for (int i = 0; i < MAXC; ++i) {
-      const int64_t c = lane + (int64_t)i * 64;
-      int q[8];
-#pragma unroll
-      for (int e = 0; e < 8; ++e) q[e] = code_of<ZP, PRE>(to_f32<DT>(half_bits(v[i], e)), mul, zp);
-      if (c < nch) cp[c] = (u32x2){pack4(q[0], q[1], q[2], q[3]), pack4(q[4], q[5], q[6], q[7])};
-    }
-  };
-  if (!ZP && zp != 0) put(std::true_type());  // uniform per row, as above
-  else put(std::false_type());
+  for (int i = 0; i < MAXC; ++i) {
+    const int64_t c = lane + (int64_t)i * 64;
+    u32x2 pk;
+    pk[0] = pack_codes16(zp_code_pair16<DT>(v[i][0], mul, zp2), zp_code_pair16<DT>(v[i][1], mul, zp2));
+    pk[1] = pack_codes16(zp_code_pair16<DT>(v[i][2], mul, zp2), zp_code_pair16<DT>(v[i][3], mul, zp2));
+    if (c < nch) cp[c] = pk;
+  }
 }
 
 // --------------------------------------------------------- column-wise ----
@@ -464,15 +498,25 @@ hipError_t launch_vw_t(const uint16_t* X, int64_t R, int64_t C, int axis, int8_t
   if (axis == 0) {  // one vector per row
     if (R <= 0) return hipSuccess;
     const dim3 grid((unsigned)((R + 3) / 4));
-    // the register kernel reads chunk 0 of every row unconditionally: C >= 8
-    const bool reg = vec && C > 0;
-    if (reg && C <= 512 * 2)
-      vw_rows_reg_kernel<DT, ZP, 2><<<grid, 256, 0, s>>>(X, R, C, codes, scale, zp);
-    else if (reg && C <= 512 * 8)
-      vw_rows_reg_kernel<DT, ZP, 8><<<grid, 256, 0, s>>>(X, R, C, codes, scale, zp);
-    else if (reg && C <= 512 * 24)
-      vw_rows_reg_kernel<DT, ZP, 24><<<grid, 256, 0, s>>>(X, R, C, codes, scale, zp);
-    else if (vec)
+    // zero-point rows held in registers (absmax per row runs the weight
+    // quantiser, above); the kernel reads chunk 0 of every row
+    // unconditionally: C >= 8
+    if constexpr (ZP) {
+      const bool reg = vec && C > 0;
+      if (reg && C <= 512 * 2) {
+        vw_rows_zp_kernel<DT, 2><<<grid, 256, 0, s>>>(X, R, C, codes, scale, zp);
+        return hipGetLastError();
+      }
+      if (reg && C <= 512 * 8) {
+        vw_rows_zp_kernel<DT, 8><<<grid, 256, 0, s>>>(X, R, C, codes, scale, zp);
+        return hipGetLastError();
+      }
+      if (reg && C <= 512 * 24) {
+        vw_rows_zp_kernel<DT, 24><<<grid, 256, 0, s>>>(X, R, C, codes, scale, zp);
+        return hipGetLastError();
+      }
+    }
+    if (vec)
       vw_rows_kernel<DT, ZP, 1><<<grid, 256, 0, s>>>(X, R, C, codes, scale, zp);
     else
       vw_rows_kernel<DT, ZP, 0><<<grid, 256, 0, s>>>(X, R, C, codes, scale, zp);

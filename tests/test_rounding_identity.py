@@ -10,7 +10,9 @@ facts, and show that no fp16 or bf16 input can produce that value, so the codes
 are the same either way.
 
 They also keep the alternative the kernels used before: with mantissa bit 0 of
-v cleared first, fl32(v' + 0.5) is exact for every v in range.
+v cleared first, fl32(v' + 0.5) is exact for every v in range.  The
+zero-point codes use that form, for |v| <= 254 (their scale is 254 / range,
+for which the trap is not ruled out): the last two tests pin it there.
 """
 import numpy as np
 
@@ -80,3 +82,24 @@ def test_no_bf16_input_reaches_the_trap():
 
 def test_plain_add_half_has_the_trap():
     assert np.trunc(TRAP + np.float32(0.5)) == 1.0   # the rounded sum reaches 1 at the trap
+
+
+def test_cleared_bit_zero_keeps_every_tie():
+    """With mantissa bit 0 cleared, v' = v or v less one ulp; floor(v' + 0.5)
+    differs from floor(v + 0.5) only if v is a tie k + 0.5 with that bit set.
+    No tie below 256 has it set, so the exact-sum form is unchanged too."""
+    ties = (np.arange(256, dtype=np.float64) + 0.5).astype(np.float32)
+    assert np.array_equal((ties.astype(np.float64) - np.arange(256)), np.full(256, 0.5))  # exact ties
+    assert not np.any(ties.view(np.uint32) & np.uint32(1))
+
+
+def test_half_away_identity_zero_point_range():
+    """floor(fl32(v' + 0.5)) == floor(v + 0.5) for every float32 in [127.5, 256]
+    (v' = v with mantissa bit 0 cleared; [0, 127.5] is the first test)."""
+    lo = int(np.float32(127.5).view(np.uint32))
+    hi = int(np.float32(256.0).view(np.uint32))
+    b = np.arange(lo, hi + 1, dtype=np.uint32)
+    v = b.view(np.float32)
+    ref = np.floor(v.astype(np.float64) + 0.5)
+    w = (b & np.uint32(0xFFFFFFFE)).view(np.float32) + np.float32(0.5)
+    assert np.array_equal(np.trunc(w).astype(np.float64), ref)
