@@ -107,16 +107,19 @@ __global__ __launch_bounds__(1024) void scan_outliers_full_kernel(
 
 // Many rows (K % 8 == 0): the 1024-thread strip workgroup above over a range
 // of rows, its final words ORed into the bitmap (non-zero ones only).  A grid
-// of about one workgroup per compute unit keeps the atomics few (1024
+// of about two workgroups per compute unit keeps the atomics few (1024
 // single-pass workgroups of four waves took 12.4 against 10.0 us at 4096 x
-// 4096 fp16), and sixteen waves of eight rows each keep 128 KiB of loads in
-// flight per compute unit: 4096 x 4096 fp16 7.85 us, 4096 x 12288 18.7 us,
-// against 8.2 and 20.1 us with four waves per workgroup.
+// 4096 fp16), and sixteen waves of four rows per batch keep 128 KiB of loads
+// in flight per compute unit: 4096 x 4096 fp16 7.4 us, 4096 x 12288 18.3 us,
+// against 7.85 and 18.9 us with eight rows per batch and one workgroup per
+// compute unit, and 8.2 and 20.1 us with four waves per workgroup.
+constexpr int SCAN_WIDE_RPT = 4;
+
 template <int DT>
 __global__ __launch_bounds__(1024) void scan_outliers_wide_kernel(
     const uint16_t* __restrict__ X, int64_t T, int64_t K, float tau, uint32_t* __restrict__ bitmap,
     int rows_per_block) {
-  constexpr int RPT = 8;  // rows per batch of loads
+  constexpr int RPT = SCAN_WIDE_RPT;  // rows per batch of loads
   __shared__ uint32_t s_m[16][4][64];
   const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
   const int64_t nch = K >> 3;
@@ -170,10 +173,10 @@ hipError_t launch_scan_outliers(int dt, const void* X, int64_t T, int64_t K, flo
   }
   if ((K & 7) == 0) {
     const int64_t gx = (K / 8 + 63) / 64;
-    // rows per workgroup: at least one batch of 128 (16 waves x 8 rows),
-    // else as many as make about one workgroup per compute unit
-    const int64_t gy_want = std::max<int64_t>(1, 256 / gx);
-    const int64_t rows = std::max<int64_t>(128, (T + gy_want - 1) / gy_want);
+    // rows per workgroup: at least one batch (16 waves x SCAN_WIDE_RPT rows),
+    // else as many as make about two workgroups per compute unit
+    const int64_t gy_want = std::max<int64_t>(1, 512 / gx);
+    const int64_t rows = std::max<int64_t>(16 * SCAN_WIDE_RPT, (T + gy_want - 1) / gy_want);
     const int64_t gy = (T + rows - 1) / rows;
     dim3 grid((unsigned)gx, (unsigned)gy);
     if (dt == DT_F16)
