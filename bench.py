@@ -29,10 +29,18 @@ The same number of steps then runs again in up to 10 blocks with one event
 pair each; "dispersion" gives the 10th, 50th and 90th percentiles of the
 blocks' per-step times.
 
-"achievable" holds two measured ceilings beside the nominal peaks: the rate
-of a loop of int8 matrix-core instructions on register operands and the
-bytes per second of a plain 1 GiB device copy; each roofline's
-"frac_of_achievable" divides its achieved rate by the ceiling of its unit.
+"achievable" holds measured ceilings beside the nominal peaks: the rate of
+a loop of int8 matrix-core instructions on register operands, once with
+every operand byte 1 and once with pseudo-random operands (the board's clock
+under matrix load depends on how much the operands switch; a GEMM's switch
+like random ones), and the bytes per second of a plain 1 GiB device copy;
+each roofline's "frac_of_achievable" divides its achieved rate by the
+random-operand loop's rate (int8) or the copy's (HBM).
+
+--vendor instead times the vendor's GEMMs on the workload's shape (the int8
+product through torch._int_mm and an fp8 e4m3 product through
+torch._scaled_mm, both hipBLASLt) beside this library's forward, each after
+the same settling, and prints one JSON line of the three.
 
 Prints one JSON line on stdout.  `value` is the effective throughput
 2*T*N*K / t in TOPS.  `roofline` describes the kernel with the largest average
@@ -79,6 +87,9 @@ def parse():
     p.add_argument("--api", choices=["binding", "module", "graph"], default="binding",
                    help="how a step is issued: the C-ABI binding, the Linear8bitLt module, "
                         "or a HIP graph of the binding's launches captured once per input copy")
+    p.add_argument("--vendor", action="store_true",
+                   help="time the vendor's int8 and fp8 GEMMs (hipBLASLt through torch) on the workload's "
+                        "shape beside this library's forward, and exit")
     p.add_argument("--copy-mib", type=float, default=0.0,
                    help="instead of the benchmark, run 10 plain device-to-device copies of this "
                         "many MiB (the calibration for HBM byte counters) and exit")
@@ -149,25 +160,33 @@ def measured_traffic(workload, kernel):
 def achievable_peaks():
     """Measured ceilings beside the nominal peaks: the int8 matrix cores in a
     loop on register operands (no memory traffic; run long enough for the
-    board's clock under sustained matrix load to settle) and a plain 1 GiB
-    device-to-device copy (bytes read plus bytes written per second)."""
+    board's clock under sustained matrix load to settle), once with every
+    operand byte 1 and once with pseudo-random operands that switch like a
+    GEMM's (the board's clock under matrix load depends on the values), and a
+    plain 1 GiB device-to-device copy (bytes read plus bytes written per
+    second)."""
     import torch
     import bit_quantized_matmul_amd as B
     iters = 4096  # about a millisecond per launch
-    sink, ops = B.lli8_mfma_i8_loop(iters)
-    torch.cuda.synchronize()
-    expect = ((4096 * iters + 2 ** 31) % 2 ** 32) - 2 ** 31
-    if int(sink[0].item()) != expect or int(sink[-1].item()) != expect:
-        raise RuntimeError("int8 matrix-core loop returned a wrong sum")
-    for _ in range(100):
-        B.lli8_mfma_i8_loop(iters, sink)
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    e0.record()
-    for _ in range(20):
-        B.lli8_mfma_i8_loop(iters, sink)
-    e1.record()
-    torch.cuda.synchronize()
-    mfma_tops = ops * 20 / (e0.elapsed_time(e1) * 1e-3) / 1e12
+    res = {}
+    for pattern, key in ((0, "mfma_i8_loop_ones"), (1, "mfma_i8_loop_random")):
+        sink, ops = B.lli8_mfma_i8_loop(iters, pattern=pattern)
+        torch.cuda.synchronize()
+        if pattern == 0:
+            expect = ((4096 * iters + 2 ** 31) % 2 ** 32) - 2 ** 31
+            if int(sink[0].item()) != expect or int(sink[-1].item()) != expect:
+                raise RuntimeError("int8 matrix-core loop returned a wrong sum")
+        for _ in range(100):
+            B.lli8_mfma_i8_loop(iters, sink, pattern=pattern)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(20):
+            B.lli8_mfma_i8_loop(iters, sink, pattern=pattern)
+        e1.record()
+        torch.cuda.synchronize()
+        tops = ops * 20 / (e0.elapsed_time(e1) * 1e-3) / 1e12
+        res[key + "_tops"] = round(tops, 1)
+        res[key + "_frac"] = round(tops / INT8_PEAK_TOPS, 4)
     n = 1 << 30
     src = torch.empty(n, dtype=torch.uint8, device="cuda").fill_(1)
     dst = torch.empty_like(src)
@@ -181,16 +200,18 @@ def achievable_peaks():
     copy_gbs = 2.0 * n * 10 / (e0.elapsed_time(e1) * 1e-3) / 1e9
     del src, dst
     torch.cuda.empty_cache()
-    return {"mfma_i8_loop_tops": round(mfma_tops, 1), "mfma_i8_loop_frac": round(mfma_tops / INT8_PEAK_TOPS, 4),
-            "hbm_copy_gbs": round(copy_gbs, 1), "hbm_copy_frac": round(copy_gbs / HBM_PEAK_GBS, 4)}
+    res["hbm_copy_gbs"] = round(copy_gbs, 1)
+    res["hbm_copy_frac"] = round(copy_gbs / HBM_PEAK_GBS, 4)
+    return res
 
 
 def frac_of_achievable(roof, ach):
-    """A roofline's achieved rate against the measured ceiling of its unit (int8 and HBM only)."""
+    """A roofline's achieved rate against the measured ceiling of its unit (int8
+    and HBM only): for int8, the matrix-core loop on pseudo-random operands."""
     if ach is None:
         return None
     if roof["bound"] == "mfma" and roof["peak"] == INT8_PEAK_TOPS:
-        return round(roof["achieved"] / ach["mfma_i8_loop_tops"], 4)
+        return round(roof["achieved"] / ach["mfma_i8_loop_random_tops"], 4)
     if roof["bound"] == "hbm":
         return round(roof["achieved"] / ach["hbm_copy_gbs"], 4)
     return None
@@ -321,6 +342,95 @@ def bench_vectorwise(args):
         line["cpu_baseline"] = {"value": round(alg / tc / 1e9, 3), "unit": "GB/s", "cores": 1, "kind": "oracle",
                                 "sample": f"full matrix (decoded to float32 beforehand); {len(times)} calls, "
                                           f"mean {tc * 1e3:.1f} ms per call"}
+    print(json.dumps(line), flush=True)
+
+
+def bench_vendor(args):
+    """The vendor's GEMMs on the workload's shape beside this library's
+    forward: torch._int_mm (int8 x int8 -> int32) on the workload's own codes
+    CA and CB, and torch._scaled_mm in fp8 e4m3 (unit scales, bf16 out) on X
+    and W cast to fp8.  Same protocol for each: operands rotated over copies
+    of >= --rotate-mib, --settle-ms of untimed calls, --warmup calls, then
+    --steps calls between one event pair."""
+    import numpy as np
+    import torch
+    import bit_quantized_matmul_amd as B
+    from workloads import config_case
+    case = config_case(args.workload)
+    dev = torch.device("cuda:0")
+    dt = torch.float16 if case.dtype == "f16" else torch.bfloat16
+    T, K, N = case.T, case.K, case.N
+    X0 = torch.from_numpy(np.ascontiguousarray(case.X).view(np.int16)).view(dt).to(dev)
+    W0 = torch.from_numpy(np.ascontiguousarray(case.W).view(np.int16)).view(dt).to(dev)
+    bias = None if case.bias is None else torch.from_numpy(np.ascontiguousarray(case.bias).view(np.int16)).view(dt).to(dev)
+    CB0, SCB0 = B.lli8_quant_weight_rowwise(W0)
+    R = max(2, -(-int(args.rotate_mib * 2 ** 20) // (N * K)))
+    CBs = [CB0] + [CB0.clone() for _ in range(R - 1)]
+    SCBs = [SCB0] + [SCB0.clone() for _ in range(R - 1)]
+    ws = B.Workspace(T, K, N, dt, dev)
+    out = torch.empty((T, N), dtype=dt, device=dev)
+    B.lli8_int8_linear(X0, CB0, SCB0, bias, case.threshold, out=out, ws=ws)
+    CA = ws.CA.clone()
+
+    def timed(fn):
+        t0, n = time.perf_counter(), 0
+        while (time.perf_counter() - t0) * 1e3 < args.settle_ms:
+            for _ in range(4):
+                fn(n)
+                n += 1
+            torch.cuda.synchronize()
+        for i in range(args.warmup):
+            fn(i)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record()
+        for i in range(args.steps):
+            fn(i)
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / args.steps
+
+    ops = 2.0 * T * N * K
+    res = {}
+    res["lli8_forward_ms"] = timed(lambda i: B.lli8_int8_linear(X0, CBs[i % R], SCBs[i % R], bias, case.threshold,
+                                                                out=out, ws=ws))
+    B.lli8_trace_enable(True)
+    B.lli8_trace_read()
+    g = []
+    for i in range(args.steps):
+        B.lli8_int8_linear(X0, CBs[i % R], SCBs[i % R], bias, case.threshold, out=out, ws=ws)
+        g += [ms for k, ms in B.lli8_trace_read() if k == "int8_gemm"]
+    torch.cuda.synchronize()
+    B.lli8_trace_enable(False)
+    res["lli8_int8_gemm_kernel_ms"] = sum(g) / len(g) if g else None
+    try:
+        res["vendor_int8_ms"] = timed(lambda i: torch._int_mm(CA, CBs[i % R].t()))
+    except RuntimeError as ex:
+        res["vendor_int8_ms"] = None
+        res["vendor_int8_error"] = str(ex).splitlines()[0][:160]
+    del CBs, SCBs
+    torch.cuda.empty_cache()
+    try:
+        f8 = torch.float8_e4m3fn
+        A8 = X0.to(f8)
+        W8s = [W0.to(f8) for _ in range(R)]
+        one = torch.ones((), device=dev)
+        res["vendor_fp8_ms"] = timed(lambda i: torch._scaled_mm(A8, W8s[i % R].t(), scale_a=one, scale_b=one,
+                                                                out_dtype=torch.bfloat16))
+    except RuntimeError as ex:
+        res["vendor_fp8_ms"] = None
+        res["vendor_fp8_error"] = str(ex).splitlines()[0][:160]
+    line = {"metric": "vendor GEMMs beside the LLM.int8 forward, ms per call and fraction of the 5033.2 "
+                      "TOP/s int8 / fp8 dense peak",
+            "config": {"workload": args.workload, "T": T, "K": K, "N": N, "act_dtype": case.dtype,
+                       "copies_rotated": R, "steps": args.steps, "settle_ms": args.settle_ms}}
+    for k, v in res.items():
+        if k.endswith("_ms"):
+            line[k] = None if v is None else round(v, 5)
+            if v is not None:
+                line[k[:-3] + "_frac"] = round(ops / (v * 1e-3) / 1e12 / INT8_PEAK_TOPS, 4)
+        else:
+            line[k] = v
     print(json.dumps(line), flush=True)
 
 
@@ -520,6 +630,9 @@ def main():
         return
     if args.vectorwise:
         bench_vectorwise(args)
+        return
+    if args.vendor:
+        bench_vendor(args)
         return
 
     import torch

@@ -97,7 +97,7 @@ def lib() -> ctypes.CDLL:
     L.lli8_last_error.restype = ctypes.c_char_p
     L.lli8_version.argtypes = []
     L.lli8_version.restype = ctypes.c_char_p
-    L.lli8_mfma_i8_loop.argtypes = [i64, vp, ctypes.POINTER(ctypes.c_double), vp]
+    L.lli8_mfma_i8_loop.argtypes = [i64, i32, vp, ctypes.POINTER(ctypes.c_double), vp]
     L.lli8_mfma_i8_loop.restype = i32
     L.lli8_mfma_i8_loop_sink_ints.argtypes = []
     L.lli8_mfma_i8_loop_sink_ints.restype = ctypes.c_size_t
@@ -258,11 +258,13 @@ def lli8_recover_weight(CB, SCB, dtype=None, W=None, stream=None):
     return W
 
 
-def lli8_mfma_i8_loop(iters: int, sink=None, device=None, stream=None):
+def lli8_mfma_i8_loop(iters: int, sink=None, device=None, stream=None, pattern: int = 0):
     """Calibration (not a step of the method): a loop of int8 matrix-core
     instructions on register operands, one workgroup per compute unit.
-    Returns (sink, ops): sink int32 [lli8_mfma_i8_loop_sink_ints()], every
-    entry (4096 * iters) mod 2^32 once the launch is done; ops the int8
+    pattern 0: every operand byte 1; pattern 1: pseudo-random operand bytes
+    (their definition is in the C header).  Returns (sink, ops): sink int32
+    [lli8_mfma_i8_loop_sink_ints()], thread t's accumulator sum once the
+    launch is done ((4096 * iters) mod 2^32 for pattern 0); ops the int8
     operations the launch performs."""
     torch = _torch()
     n = int(lib().lli8_mfma_i8_loop_sink_ints())
@@ -272,7 +274,8 @@ def lli8_mfma_i8_loop(iters: int, sink=None, device=None, stream=None):
         sink = torch.empty((n,), dtype=torch.int32, device=dev)
     _arg(sink, "sink", dev, torch.int32, n)
     ops = ctypes.c_double(0.0)
-    _check(lib().lli8_mfma_i8_loop(int(iters), _ptr(sink), ctypes.byref(ops), _stream(dev, stream)))
+    _check(lib().lli8_mfma_i8_loop(int(iters), int(pattern), _ptr(sink), ctypes.byref(ops),
+                                   _stream(dev, stream)))
     return sink, ops.value
 
 

@@ -292,15 +292,16 @@ size_t lli8_mfma_i8_loop_sink_ints(void) {
   return e == hipSuccess ? (size_t)cus * 512 : 0;
 }
 
-lli8_status_t lli8_mfma_i8_loop(int64_t iters, int32_t* sink, double* ops, void* stream) {
+lli8_status_t lli8_mfma_i8_loop(int64_t iters, int pattern, int32_t* sink, double* ops, void* stream) {
   if (iters < 1) return fail(LLI8_ERR_SHAPE, "iters must be at least 1, got %lld", (long long)iters);
+  if (pattern != 0 && pattern != 1) return fail(LLI8_ERR_UNSUPPORTED, "operand pattern must be 0 or 1, got %d", pattern);
   REQUIRE(sink, "sink");
   if (ops == nullptr) return fail(LLI8_ERR_NULL, "ops is NULL");
   hipError_t e;
   const int cus = current_device_cus(&e);
   if (e != hipSuccess) return hip_status(e, "device query");
   hipStream_t s = static_cast<hipStream_t>(stream);
-  TRY(hip_status(lli8::launch_mfma_i8_loop(iters, cus, sink, s), "mfma loop launch"));
+  TRY(hip_status(lli8::launch_mfma_i8_loop(iters, pattern, cus, sink, s), "mfma loop launch"));
   // 8 waves x 8 instructions x 2 * 32^3 operations per iteration per workgroup
   *ops = (double)cus * 8.0 * 8.0 * 65536.0 * (double)iters;
   return LLI8_OK;

@@ -54,7 +54,7 @@ inline bool stream_gemm_route(int64_t T, int64_t N, int64_t K) {
 }
 
 // Calibration loop of int8 matrix-core instructions (lli8_calib.hip).
-hipError_t launch_mfma_i8_loop(int64_t iters, int blocks, int32_t* sink, hipStream_t s);
+hipError_t launch_mfma_i8_loop(int64_t iters, int pattern, int blocks, int32_t* sink, hipStream_t s);
 
 // W = dtype(fl32(fl32(CB * SCB) / 127)) for a whole [N, K] weight.
 hipError_t launch_recover_weight(int dt, const int8_t* CB, const float* SCB, int64_t N, int64_t K, void* W,

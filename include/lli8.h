@@ -253,17 +253,26 @@ lli8_status_t lli8_quant_vectorwise(const void* X, int64_t R, int64_t C, lli8_dt
  * on this board with nothing else limiting them, for comparing the GEMM with
  * an achievable peak beside the nominal one.  One 512-thread workgroup per
  * compute unit; each of its eight waves issues 8 * iters
- * v_mfma_i32_32x32x32_i8 on operands held in registers (every operand byte
- * 1, so each thread's accumulators sum to 4096 * iters, modulo 2^32, which it
- * writes to sink[thread]).
- *   sink  device int32 buffer of lli8_mfma_i8_loop_sink_ints() entries
- *         (512 per compute unit of the current device), 16-byte aligned
- *   ops   host: receives the int8 operations the launch performs
- *         (2 * 32^3 per instruction)
+ * v_mfma_i32_32x32x32_i8 on operands held in registers, in eight chains of
+ * accumulators; thread t writes the sum of its accumulators (modulo 2^32) to
+ * sink[t].
+ *   pattern  0: every operand byte 1 (each thread's sum is 4096 * iters);
+ *            1: pseudo-random bytes, the clock the board holds when the
+ *            operands switch as a GEMM's do.  Dword e (0..3) of thread t's
+ *            A operand j (0..3) is mix(32 t + 4 j + e), of its B operand j
+ *            mix(32 t + 16 + 4 j + e), where mix(x) is: x ^= x >> 16;
+ *            x *= 0x7feb352d; x ^= x >> 15; x *= 0x846ca68b; x ^= x >> 16
+ *            (32-bit unsigned arithmetic); chain c (0..7) multiplies A
+ *            operand c % 4 by B operand c / 2.
+ *   sink     device int32 buffer of lli8_mfma_i8_loop_sink_ints() entries
+ *            (512 per compute unit of the current device), 16-byte aligned
+ *   ops      host: receives the int8 operations the launch performs
+ *            (2 * 32^3 per instruction)
  * Asynchronous on `stream`.  Errors: LLI8_ERR_SHAPE (iters < 1),
- * LLI8_ERR_NULL, LLI8_ERR_ALIGN, LLI8_ERR_HIP.
+ * LLI8_ERR_UNSUPPORTED (pattern not 0 or 1), LLI8_ERR_NULL, LLI8_ERR_ALIGN,
+ * LLI8_ERR_HIP.
  */
-lli8_status_t lli8_mfma_i8_loop(int64_t iters, int32_t* sink, double* ops, void* stream);
+lli8_status_t lli8_mfma_i8_loop(int64_t iters, int pattern, int32_t* sink, double* ops, void* stream);
 size_t lli8_mfma_i8_loop_sink_ints(void);
 
 /*

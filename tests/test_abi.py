@@ -166,10 +166,12 @@ def test_validation_mfma_loop():
     L = _lib().lib()
     ops = ctypes.c_double(0.0)
     f = L.lli8_mfma_i8_loop
-    assert f(0, FAKE, ctypes.byref(ops), None) == 2           # iters < 1
-    assert f(8, None, ctypes.byref(ops), None) == 1           # sink NULL
-    assert f(8, FAKE + 4, ctypes.byref(ops), None) == 4       # sink misaligned
-    assert f(8, FAKE, None, None) == 1                        # ops NULL
+    assert f(0, 0, FAKE, ctypes.byref(ops), None) == 2           # iters < 1
+    assert f(8, 2, FAKE, ctypes.byref(ops), None) == 6           # unknown operand pattern
+    assert f(8, -1, FAKE, ctypes.byref(ops), None) == 6
+    assert f(8, 0, None, ctypes.byref(ops), None) == 1           # sink NULL
+    assert f(8, 1, FAKE + 4, ctypes.byref(ops), None) == 4       # sink misaligned
+    assert f(8, 0, FAKE, None, None) == 1                        # ops NULL
 
 
 def test_workspace_bytes_and_carve():
