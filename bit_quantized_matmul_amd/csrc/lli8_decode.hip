@@ -36,6 +36,22 @@ constexpr int FD_MAXK = FD_CW * 64 * 8;       // 4096: one 8-column chunk per ac
 constexpr int FD_MAXW = FD_MAXK / 32;         // bitmap words
 constexpr int FD_MPL = FD_MAXK / FD_LW / 64;  // MFMAs (64 columns each) per weight wave: 16
 constexpr int FD_OUT_LDS = 64;                // outlier columns staged in LDS; more read global memory
+// An arrival count in LDS, for a meeting that the weight waves must not
+// join: a wave issuing its weight loads can stall at issue for as long as
+// the memory pipeline is full, and a workgroup barrier would hold every
+// other wave behind it.  LDS operations of one wave are performed in
+// order, so the data a wave writes before its count is seen by any wave
+// that has read the count; the empty asm statements keep the compiler from
+// moving LDS accesses across the count operations.
+__device__ __forceinline__ void lds_arrive(uint32_t* cnt, int lane) {
+  asm volatile("" ::: "memory");
+  if (lane == 0) __hip_atomic_fetch_add(cnt, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+  asm volatile("" ::: "memory");
+}
+__device__ __forceinline__ void lds_wait_count(uint32_t* cnt, uint32_t n) {
+  while (__hip_atomic_load(cnt, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP) < n) __builtin_amdgcn_s_sleep(1);
+  asm volatile("" ::: "memory");
+}
 
 // Cross-lane moves without LDS: DPP within a row of 16 lanes, the gfx950
 // permlane swaps across rows.
@@ -122,6 +138,7 @@ __global__ __launch_bounds__(FD_THREADS, 1) void decode_fused_kernel(
   __shared__ float s_sca[16];
   __shared__ int s_nout;
   __shared__ v4i s_red[FD_LW - 1][64];
+  __shared__ uint32_t s_b1;  // activation waves past their statistics
   __shared__ float s_ow[FD_OUT_LDS][16];  // recovered weights of the outlier columns, this block
   __shared__ float s_ox[FD_OUT_LDS][16];  // X values of the outlier columns
 
@@ -131,10 +148,18 @@ __global__ __launch_bounds__(FD_THREADS, 1) void decode_fused_kernel(
   const int W = (K + 31) >> 5;
   const int blk0 = wg;  // the grid never exceeds the number of blocks
 
-  // Both roles pass the same sequence of workgroup barriers: B1 (per-wave
-  // row maxima, bitmap), B2 (codes, outlier index list, X values and
-  // recovered weights of the outlier columns, row scales), then per block B3
-  // (partial tiles) and B4 (epilogue done).
+  // Both roles pass the same sequence of workgroup barriers: B0 (the
+  // arrival count is zero, and the activation waves' X loads are issued,
+  // not waited for, so they reach memory ahead of the weight stream), B2
+  // (codes, outlier index list, X values and recovered weights of the
+  // outlier columns, row scales), then per block B3 (partial tiles) and B4
+  // (epilogue done).  B1 (per-wave row maxima, bitmap) is an arrival count
+  // of the activation waves alone; the weight waves issue their stream
+  // right after B0 and read the count only once it is issued.
+  if (tid == 0) {
+    s_b1 = 0u;
+    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): zeroed before B0
+  }
   if (w < FD_CW) {
     // ------------------------------------------------ activation waves ----
     const uint32_t t16 = magnitude_threshold<DT>(tau);  // |x| > tau  <=>  (bits & 0x7FFF) > t16
@@ -154,6 +179,7 @@ __global__ __launch_bounds__(FD_THREADS, 1) void decode_fused_kernel(
         xr[t] = *reinterpret_cast<const u32x4*>(xc + (int64_t)tt * K);
       }
     }
+    __builtin_amdgcn_s_barrier();  // B0 (no wait for the X loads)
 
     // 2. statistics: column maxima of the 15-bit magnitudes over the 16 rows
     // (two columns per dword) and, in the same pass, each row's maximum over
@@ -203,7 +229,8 @@ __global__ __launch_bounds__(FD_THREADS, 1) void decode_fused_kernel(
       const uint32_t q1 = wave_max8_u16x2(pr, lane);
       if ((lane & 7) == 0) s_wmax[w][lane >> 3] = q1;
     }
-    __syncthreads();  // B1
+    lds_arrive(&s_b1, lane);  // B1 among the activation waves
+    lds_wait_count(&s_b1, FD_CW);
 
     // row scales, in every wave: lane l takes rows 2p, 2p + 1 with p = l & 7
     const bool any = __ballot(lane < FD_CW && s_wany[lane & (FD_CW - 1)] != 0u) != 0;
@@ -332,11 +359,14 @@ __global__ __launch_bounds__(FD_THREADS, 1) void decode_fused_kernel(
         }
       }
     };
-    // The weight loads are issued after B1: a wave issuing them stalls until
-    // queue space frees up, and B1 must not wait for that.  By then the
-    // activation loads have all returned.
-    __syncthreads();  // B1
+    // The weight loads are issued right after B0, behind the activation
+    // waves' X loads; a wave issuing them stalls until queue space frees up,
+    // so the weight waves wait for the activation waves (B1) only after that
+    // (issuing them later, once some or all activation waves hold their X
+    // rows, measured the same).
+    __builtin_amdgcn_s_barrier();  // B0
     load_cb(blk0);
+    lds_wait_count(&s_b1, FD_CW);  // B1: bitmap and row maxima are in LDS
     const bool any = __ballot(lane < FD_CW && s_wany[lane & (FD_CW - 1)] != 0u) != 0;
     int n_out = 0;
     uint32_t pp = 0u;
