@@ -112,7 +112,7 @@ __device__ __forceinline__ uint32_t bitmap_prefix(const uint32_t* s_bm, int W, i
   const uint32_t w1 = (2 * lane + 1 < W) ? s_bm[2 * lane + 1] : 0u;
   const int cnt = __popc(w0) + __popc(w1);
   const int incl = wave_incl_scan(cnt);
-  total = __shfl(incl, 63, WAVE);
+  total = __builtin_amdgcn_readlane(incl, 63);
   const uint32_t p0 = (uint32_t)(incl - cnt);
   return p0 | ((p0 + (uint32_t)__popc(w0)) << 16);
 }

@@ -185,14 +185,18 @@ __device__ __forceinline__ uint32_t wave_or(uint32_t v) {
   return v;
 }
 
-// Inclusive prefix sum across the wave.
+// Inclusive prefix sum across the wave, in registers (DPP, no LDS round
+// trips): within each row of 16 lanes by row shifts of 1, 2, 4 and 8 lanes
+// (lanes shifted in from outside the row read 0), then across rows by the
+// gfx9 row broadcasts: lane 15 of rows 0 and 2 into rows 1 and 3, then lane
+// 31 (the total of rows 0-1) into rows 2 and 3.
 __device__ __forceinline__ int wave_incl_scan(int v) {
-  const int lane = threadIdx.x & (WAVE - 1);
-#pragma unroll
-  for (int off = 1; off < WAVE; off <<= 1) {
-    int u = __shfl_up(v, off, WAVE);
-    if (lane >= off) v += u;
-  }
+  v += __builtin_amdgcn_update_dpp(0, v, 0x111, 0xF, 0xF, true);   // row_shr:1
+  v += __builtin_amdgcn_update_dpp(0, v, 0x112, 0xF, 0xF, true);   // row_shr:2
+  v += __builtin_amdgcn_update_dpp(0, v, 0x114, 0xF, 0xF, true);   // row_shr:4
+  v += __builtin_amdgcn_update_dpp(0, v, 0x118, 0xF, 0xF, true);   // row_shr:8
+  v += __builtin_amdgcn_update_dpp(0, v, 0x142, 0xA, 0xF, false);  // row_bcast:15, rows 1 and 3
+  v += __builtin_amdgcn_update_dpp(0, v, 0x143, 0xC, 0xF, false);  // row_bcast:31, rows 2 and 3
   return v;
 }
 
