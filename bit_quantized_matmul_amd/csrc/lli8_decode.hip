@@ -106,10 +106,12 @@ __device__ __forceinline__ uint32_t wave_max_by8_u16x2(uint32_t v) {
 }
 
 // Exclusive prefix counts of outlier bitmap words 2l and 2l + 1 (W <= 128)
-// packed as two 16-bit halves in lane l, and the total count.
-__device__ __forceinline__ uint32_t bitmap_prefix(const uint32_t* s_bm, int W, int lane, int& total) {
-  const uint32_t w0 = (2 * lane < W) ? s_bm[2 * lane] : 0u;
-  const uint32_t w1 = (2 * lane + 1 < W) ? s_bm[2 * lane + 1] : 0u;
+// packed as two 16-bit halves in lane l, and the total count; the two words
+// themselves (0 past W) are left in w0, w1.
+__device__ __forceinline__ uint32_t bitmap_prefix(const uint32_t* s_bm, int W, int lane, int& total, uint32_t& w0,
+                                                  uint32_t& w1) {
+  w0 = (2 * lane < W) ? s_bm[2 * lane] : 0u;
+  w1 = (2 * lane + 1 < W) ? s_bm[2 * lane + 1] : 0u;
   const int cnt = __popc(w0) + __popc(w1);
   const int incl = wave_incl_scan(cnt);
   total = __builtin_amdgcn_readlane(incl, 63);
@@ -139,8 +141,11 @@ __global__ __launch_bounds__(FD_THREADS, 1) void decode_fused_kernel(
   __shared__ int s_nout;
   __shared__ v4i s_red[FD_LW - 1][64];
   __shared__ uint32_t s_b1;  // activation waves past their statistics
-  __shared__ float s_ow[FD_OUT_LDS][16];  // recovered weights of the outlier columns, this block
-  __shared__ float s_ox[FD_OUT_LDS][16];  // X values of the outlier columns
+  __shared__ int8_t s_ocb[FD_OUT_LDS][16];  // CB bytes of the outlier columns, this block
+  __shared__ u32x4 s_oxc[FD_OUT_LDS][16];  // the 8-column chunk of each outlier column, all 16 rows
+  __shared__ int s_oxe[FD_OUT_LDS];        // the outlier column's place in its chunk
+  __shared__ float s_scb[16];              // weight row scales of the first block
+  __shared__ float s_osum[16][16];         // first block's 16-bit outlier product, [token][feature]
 
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int G = gridDim.x, wg = blockIdx.x;
@@ -197,12 +202,11 @@ __global__ __launch_bounds__(FD_THREADS, 1) void decode_fused_kernel(
       rm[t] = pk_max_u16(pk_max_u16(a[0], a[1]), pk_max_u16(a[2], a[3]));
     }
     const uint32_t f8 = cok ? flags8(cm, t16) : 0u;  // bit e: column 8c + e is an outlier column
-    {  // bitmap word c / 4 from the four lanes of a quad; no atomics
-      uint32_t wv = f8 << (8 * (c & 3));
-      wv |= dpp<DPP_QUAD_XOR1>(wv);
-      wv |= dpp<DPP_QUAD_XOR2>(wv);
-      if ((c & 3) == 0 && cok) s_bm[c >> 2] = wv;
-    }
+    // bitmap word c / 4 from the four lanes of a quad, held by all four; no atomics
+    uint32_t wword = f8 << (8 * (c & 3));
+    wword |= dpp<DPP_QUAD_XOR1>(wword);
+    wword |= dpp<DPP_QUAD_XOR2>(wword);
+    if ((c & 3) == 0 && cok) s_bm[c >> 2] = wword;
     const uint64_t anyw = __ballot(f8 != 0u);
     if (lane == 0) s_wany[w] = anyw != 0 ? 1u : 0u;
     if (!cok) {
@@ -267,8 +271,9 @@ __global__ __launch_bounds__(FD_THREADS, 1) void decode_fused_kernel(
       }
     }
     int n_out = 0;
-    if (any) {  // this chunk's outlier columns: their index and X values
-      const uint32_t pp = bitmap_prefix(s_bm, W, lane, n_out);
+    if (any) {  // this chunk's outlier columns: their index, and the chunk's X rows
+      uint32_t bw0, bw1;
+      const uint32_t pp = bitmap_prefix(s_bm, W, lane, n_out, bw0, bw1);
       const int word = c >> 2;  // prefix of this chunk's bitmap word, from lane word / 2 of this wave
       const uint32_t pw = (uint32_t)__shfl((int)pp, (word >> 1) & 63, WAVE);
       const uint32_t pre = (word & 1) ? (pw >> 16) : (pw & 0xFFFFu);
@@ -277,15 +282,32 @@ __global__ __launch_bounds__(FD_THREADS, 1) void decode_fused_kernel(
         const int e = __builtin_ctz(f);
         f &= f - 1u;
         const int col = 8 * c + e;
-        const int rank = (int)pre + __popc(s_bm[word] & ((1u << (col & 31)) - 1u));
+        const int rank = (int)pre + __popc(wword & ((1u << (col & 31)) - 1u));
         s_idx[rank] = col;
-        if (rank < FD_OUT_LDS) {
+        if (rank < FD_OUT_LDS) {  // whole rows of the chunk, no per-row selects; the reader picks value e
+          s_oxe[rank] = e;
 #pragma unroll
-          for (int t = 0; t < 16; ++t) s_ox[rank][t] = (t < T) ? to_f32<DT>(half_bits(xr[t], e)) : 0.0f;
+          for (int t = 0; t < 16; ++t) s_oxc[rank][t] = xr[t];
         }
       }
     }
     __syncthreads();  // B2
+
+    // the first block's 16-bit outlier product over the staged columns, one
+    // (token, feature) per thread while the weight waves run the int8
+    // products; weight wave 0 reads it after B3
+    if (any && tid < 256) {
+      const int t = tid >> 4, n = tid & 15;
+      const float sc = s_scb[n];
+      const int n_lds = min(n_out, FD_OUT_LDS);
+      float o = 0.0f;
+      for (int p = 0; p < n_lds; ++p) {
+        // recovered weight dtype(fl32(fl32(CB * SCB) / 127))
+        const float wv = to_f32<DT>(from_f32<DT>(div127((float)s_ocb[p][n] * sc)));
+        o += to_f32<DT>(reinterpret_cast<const uint16_t*>(&s_oxc[p][t])[s_oxe[p]]) * wv;
+      }
+      s_osum[t][n] = o;
+    }
 
     // side outputs: CA shared out over the grid, the small ones by workgroup 0
     {
@@ -336,26 +358,27 @@ __global__ __launch_bounds__(FD_THREADS, 1) void decode_fused_kernel(
       scb_n = SCB[cc];
       bias_n = to_f32<DT>(bsrc[cc] & bmask);
     };
-    // recovered weights dtype(fl32(fl32(CB * SCB) / 127)) of the outlier
-    // columns of this block, from registers
-    auto stage_outlier_weights = [&](uint32_t pp) {
+    // CB bytes of the outlier columns of this block, from registers, placed by
+    // rank; the bitmap words come from the prefix pass's registers (lane L
+    // holds words 2L and 2L + 1), so no LDS read waits in this chain.  The
+    // recovery (CB * SCB) / 127 happens where the products are summed.
+    auto stage_outlier_bytes = [&](uint32_t pp, uint32_t bw0, uint32_t bw1) {
 #pragma unroll
       for (int m = 0; m < FD_MPL; ++m) {
+        const int L = lw * 16 + m;  // the lane with this m's two words (64 columns)
+        const uint32_t wa = (uint32_t)__builtin_amdgcn_readlane((int)bw0, L);
+        const uint32_t wb = (uint32_t)__builtin_amdgcn_readlane((int)bw1, L);
+        if ((wa | wb) == 0u) continue;  // no outlier column among these 64
         const int k0 = lw * 1024 + m * 64 + q * 16;
-        const int word = k0 >> 5;
-        uint32_t bits = (k0 < K) ? (s_bm[word] >> (k0 & 31)) & 0xFFFFu : 0u;
-        if (__ballot(bits != 0u) == 0) continue;  // no outlier column among these 64
-        const uint32_t pw = (uint32_t)__builtin_amdgcn_readlane((int)pp, lw * 16 + m);  // = word / 2
-        const uint32_t pre = (word & 1) ? (pw >> 16) : (pw & 0xFFFFu);
+        const uint32_t wd = (q >> 1) ? wb : wa;  // word k0 / 32 (0 past K)
+        uint32_t bits = (wd >> (k0 & 31)) & 0xFFFFu;
+        const uint32_t pw = (uint32_t)__builtin_amdgcn_readlane((int)pp, L);
+        const uint32_t pre = (q >> 1) ? (pw >> 16) : (pw & 0xFFFFu);
         while (bits) {
           const int e = __builtin_ctz(bits);
           bits &= bits - 1u;
-          const int col = k0 + e;
-          const int rank = (int)pre + __popc(s_bm[word] & ((1u << (col & 31)) - 1u));
-          if (rank < FD_OUT_LDS) {
-            const int8_t cb = (int8_t)((b[m][e >> 2] >> (8 * (e & 3))) & 0xFFu);
-            s_ow[rank][nr] = to_f32<DT>(from_f32<DT>(div127((float)cb * scb_n)));
-          }
+          const int rank = (int)pre + __popc(wd & ((1u << ((k0 & 31) + e)) - 1u));
+          if (rank < FD_OUT_LDS) s_ocb[rank][nr] = (int8_t)((b[m][e >> 2] >> (8 * (e & 3))) & 0xFFu);
         }
       }
     };
@@ -369,10 +392,11 @@ __global__ __launch_bounds__(FD_THREADS, 1) void decode_fused_kernel(
     lds_wait_count(&s_b1, FD_CW);  // B1: bitmap and row maxima are in LDS
     const bool any = __ballot(lane < FD_CW && s_wany[lane & (FD_CW - 1)] != 0u) != 0;
     int n_out = 0;
-    uint32_t pp = 0u;
+    uint32_t pp = 0u, bw0 = 0u, bw1 = 0u;
     if (any) {
-      pp = bitmap_prefix(s_bm, W, lane, n_out);
-      stage_outlier_weights(pp);
+      pp = bitmap_prefix(s_bm, W, lane, n_out, bw0, bw1);
+      stage_outlier_bytes(pp, bw0, bw1);
+      if (lw == 0 && lane < 16) s_scb[nr] = scb_n;
     }
     const int n_lds = min(n_out, FD_OUT_LDS);
     __syncthreads();  // B2
@@ -381,20 +405,23 @@ __global__ __launch_bounds__(FD_THREADS, 1) void decode_fused_kernel(
     for (int blk = blk0; blk < nblk; blk += G) {
       if (blk != blk0) {
         load_cb(blk);
-        if (any) stage_outlier_weights(pp);
+        if (any) stage_outlier_bytes(pp, bw0, bw1);
       }
-      // 16-bit outlier product (weight wave 0): for the first block the staged
-      // weights are complete since B2, so it overlaps the int8 products; for
-      // later blocks the other waves stage theirs after B4, so it waits for B3
+      // 16-bit outlier product (weight wave 0, after B3): the activation
+      // waves sum the first block's between B2 and B3; for later blocks
+      // weight wave 0 sums it itself, the CB bytes being staged after B4
       float o[4] = {0.f, 0.f, 0.f, 0.f};
+      // (rows beyond T hold row T - 1: they only feed outputs never stored)
       auto outlier_sum = [&]() {
         for (int p = 0; p < n_lds; ++p) {
-          const float wv = s_ow[p][nr];
+          // recovered weight dtype(fl32(fl32(CB * SCB) / 127)) of feature nr
+          const float wv = to_f32<DT>(from_f32<DT>(div127((float)s_ocb[p][nr] * scb_n)));
+          const int e = s_oxe[p];
 #pragma unroll
-          for (int r = 0; r < 4; ++r) o[r] += s_ox[p][4 * q + r] * wv;
+          for (int r = 0; r < 4; ++r)
+            o[r] += to_f32<DT>(reinterpret_cast<const uint16_t*>(&s_oxc[p][4 * q + r])[e]) * wv;
         }
       };
-      if (lw == 0 && blk == blk0) outlier_sum();
       v4i acc = {0, 0, 0, 0};
 #pragma unroll
       for (int h = 0; h < FD_MPL; h += 8) {  // A operands (codes of rows 0-15, the same columns), 8 reads in flight
@@ -409,7 +436,12 @@ __global__ __launch_bounds__(FD_THREADS, 1) void decode_fused_kernel(
       if (lw > 0) s_red[lw - 1][lane] = acc;
       __syncthreads();  // B3
       if (lw == 0) {
-        if (blk != blk0) outlier_sum();
+        if (blk != blk0) {
+          outlier_sum();
+        } else if (any) {
+#pragma unroll
+          for (int r = 0; r < 4; ++r) o[r] = s_osum[4 * q + r][nr];
+        }
 #pragma unroll
         for (int i = 0; i < FD_LW - 1; ++i) acc += s_red[i][lane];  // fixed order: deterministic
         // 16x16 layout: lane holds feature lane % 16, tokens 4 * (lane / 16) + r
