@@ -141,11 +141,14 @@ __global__ __launch_bounds__(FD_THREADS, 1) void decode_fused_kernel(
   __shared__ int s_nout;
   __shared__ v4i s_red[FD_LW - 1][64];
   __shared__ uint32_t s_b1;  // activation waves past their statistics
+  __shared__ uint32_t s_b2;  // activation waves done with the first block's outlier operands
   __shared__ int8_t s_ocb[FD_OUT_LDS][16];  // CB bytes of the outlier columns, this block
   __shared__ u32x4 s_oxc[FD_OUT_LDS][16];  // the 8-column chunk of each outlier column, all 16 rows
   __shared__ int s_oxe[FD_OUT_LDS];        // the outlier column's place in its chunk
   __shared__ float s_scb[16];              // weight row scales of the first block
   __shared__ float s_osum[16][16];         // first block's 16-bit outlier product, [token][feature]
+  __shared__ float s_owv[FD_OUT_LDS][16];  // first block: recovered outlier weights, [column][feature]
+  __shared__ float s_oxv[FD_OUT_LDS][16];  // outlier columns' X values, [column][token]
 
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int G = gridDim.x, wg = blockIdx.x;
@@ -163,6 +166,7 @@ __global__ __launch_bounds__(FD_THREADS, 1) void decode_fused_kernel(
   // right after B0 and read the count only once it is issued.
   if (tid == 0) {
     s_b1 = 0u;
+    s_b2 = 0u;
     __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): zeroed before B0
   }
   if (w < FD_CW) {
@@ -293,20 +297,28 @@ __global__ __launch_bounds__(FD_THREADS, 1) void decode_fused_kernel(
     }
     __syncthreads();  // B2
 
-    // the first block's 16-bit outlier product over the staged columns, one
-    // (token, feature) per thread while the weight waves run the int8
-    // products; weight wave 0 reads it after B3
-    if (any && tid < 256) {
-      const int t = tid >> 4, n = tid & 15;
-      const float sc = s_scb[n];
+    // the first block's 16-bit outlier product over the staged columns while
+    // the weight waves run the int8 products; weight wave 0 reads it after
+    // B3.  First each recovered weight dtype(fl32(fl32(CB * SCB) / 127)) and
+    // each X value once (not once per output), then, after the activation
+    // waves meet, one (token, feature) per thread, summed in column order.
+    if (any) {
       const int n_lds = min(n_out, FD_OUT_LDS);
-      float o = 0.0f;
-      for (int p = 0; p < n_lds; ++p) {
-        // recovered weight dtype(fl32(fl32(CB * SCB) / 127))
-        const float wv = to_f32<DT>(from_f32<DT>(div127((float)s_ocb[p][n] * sc)));
-        o += to_f32<DT>(reinterpret_cast<const uint16_t*>(&s_oxc[p][t])[s_oxe[p]]) * wv;
+      for (int i = tid; i < 32 * n_lds; i += FD_CW * 64) {
+        const int p = i >> 4, j = i & 15;  // items [0, 16 n_lds): weights; then X values
+        if (p < n_lds)
+          s_owv[p][j] = to_f32<DT>(from_f32<DT>(div127((float)s_ocb[p][j] * s_scb[j])));
+        else
+          s_oxv[p - n_lds][j] = to_f32<DT>(half_bits(s_oxc[p - n_lds][j], s_oxe[p - n_lds]));
       }
-      s_osum[t][n] = o;
+      lds_arrive(&s_b2, lane);
+      lds_wait_count(&s_b2, FD_CW);
+      if (tid < 256) {
+        const int t = tid >> 4, n = tid & 15;
+        float o = 0.0f;
+        for (int p = 0; p < n_lds; ++p) o += s_oxv[p][t] * s_owv[p][n];
+        s_osum[t][n] = o;
+      }
     }
 
     // side outputs: CA shared out over the grid, the small ones by workgroup 0
