@@ -138,6 +138,13 @@ def fused_many_blocks_case():
     return random_case(7, 512, 16 * 256 * 3 + 5, seed=78, n_out=2)
 
 
+def fused_many_blocks_dense_case():
+    # all 16 rows, three blocks for most workgroups; with tau 0.1 more outlier
+    # columns than the 64 staged in LDS, so later blocks also take the rest
+    # from memory
+    return random_case(16, 1024, 16 * 256 * 2 + 3, seed=79, n_out=3)
+
+
 def scratch_sizes_case():
     return random_case(300, 512, 260, seed=31, n_out=70)
 

@@ -202,6 +202,14 @@ def test_fused_decode_many_blocks_per_workgroup():
     _check_full(PC.fused_many_blocks_case())
 
 
+@pytest.mark.parametrize("tau", [3.0, 2.0, 0.1])
+def test_fused_decode_many_blocks_dense_outliers(tau):
+    """Several blocks per workgroup with many outlier columns (42 at tau 3; 510 and all
+    1024 at tau 2 and 0.1, beyond the 64 staged in LDS), so every block after the first
+    sums its 16-bit product itself."""
+    _check_full(PC.fused_many_blocks_dense_case(), tau)
+
+
 @pytest.mark.parametrize("room_chunks", ["full", 0, 1])
 def test_recovered_outlier_weights_scratch_sizes(room_chunks):
     """The recovered outlier weights come from scratch for as many 32-column
