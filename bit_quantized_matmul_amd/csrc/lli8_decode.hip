@@ -139,7 +139,7 @@ __global__ __launch_bounds__(FD_THREADS, 1) void decode_fused_kernel(
   __shared__ uint32_t s_wany[FD_CW];
   __shared__ float s_sca[16];
   __shared__ int s_nout;
-  __shared__ v4i s_red[FD_LW - 1][64];
+  __shared__ v4i s_red[FD_LW][64];  // each weight wave's int32 partial tile
   __shared__ uint32_t s_b1;  // activation waves past their statistics
   __shared__ uint32_t s_b2;  // activation waves done with the first block's outlier operands
   __shared__ int8_t s_ocb[FD_OUT_LDS][16];  // CB bytes of the outlier columns, this block
@@ -419,20 +419,22 @@ __global__ __launch_bounds__(FD_THREADS, 1) void decode_fused_kernel(
         load_cb(blk);
         if (any) stage_outlier_bytes(pp, bw0, bw1);
       }
-      // 16-bit outlier product (weight wave 0, after B3): the activation
-      // waves sum the first block's between B2 and B3; for later blocks
-      // weight wave 0 sums it itself, the CB bytes being staged after B4
-      float o[4] = {0.f, 0.f, 0.f, 0.f};
-      // (rows beyond T hold row T - 1: they only feed outputs never stored)
-      auto outlier_sum = [&]() {
+      // 16x16 layout: lane holds feature nr = lane % 16, tokens 4 q + r
+      // (r = 0 .. 3).  After B3 weight wave lw finishes token 4 q + lw of
+      // every lane's group: the four waves' int32 partials summed (exact in
+      // any order), its 16-bit outlier product, the epilogue.  The
+      // activation waves sum the first block's outlier product between B2 and
+      // B3; for later blocks each weight wave sums its token's itself over
+      // the CB bytes all four staged after B4 (rows beyond T hold row T - 1:
+      // they only feed outputs never stored).
+      auto outlier_sum = [&](int t) {
+        float o = 0.0f;
         for (int p = 0; p < n_lds; ++p) {
           // recovered weight dtype(fl32(fl32(CB * SCB) / 127)) of feature nr
           const float wv = to_f32<DT>(from_f32<DT>(div127((float)s_ocb[p][nr] * scb_n)));
-          const int e = s_oxe[p];
-#pragma unroll
-          for (int r = 0; r < 4; ++r)
-            o[r] += to_f32<DT>(reinterpret_cast<const uint16_t*>(&s_oxc[p][4 * q + r])[e]) * wv;
+          o += to_f32<DT>(reinterpret_cast<const uint16_t*>(&s_oxc[p][t])[s_oxe[p]]) * wv;
         }
+        return o;
       };
       v4i acc = {0, 0, 0, 0};
 #pragma unroll
@@ -445,37 +447,28 @@ __global__ __launch_bounds__(FD_THREADS, 1) void decode_fused_kernel(
         for (int m = 0; m < 8; ++m)
           acc = __builtin_amdgcn_mfma_i32_16x16x64_i8(am[m], __builtin_bit_cast(v4i, b[h + m]), acc, 0, 0, 0);
       }
-      if (lw > 0) s_red[lw - 1][lane] = acc;
+      s_red[lw][lane] = acc;
       __syncthreads();  // B3
-      if (lw == 0) {
-        if (blk != blk0) {
-          outlier_sum();
-        } else if (any) {
+      {
+        const int t = 4 * q + lw;
+        int32_t a = 0;
 #pragma unroll
-          for (int r = 0; r < 4; ++r) o[r] = s_osum[4 * q + r][nr];
-        }
-#pragma unroll
-        for (int i = 0; i < FD_LW - 1; ++i) acc += s_red[i][lane];  // fixed order: deterministic
-        // 16x16 layout: lane holds feature lane % 16, tokens 4 * (lane / 16) + r
+        for (int i = 0; i < FD_LW; ++i) a += s_red[i][lane][lw];
+        float o = 0.0f;
+        if (blk != blk0)
+          o = outlier_sum(t);
+        else if (any)
+          o = s_osum[t][nr];
         const int64_t col = (int64_t)blk * 16 + nr;
-        if (col < N) {
+        if (col < N && t < T) {
           for (int p = n_lds; p < n_out; ++p) {  // beyond the LDS stage: straight from memory
             const int cc = s_idx[p];
             const float wv = to_f32<DT>(from_f32<DT>(div127((float)CB[col * K + cc] * scb_n)));
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-              const int t = 4 * q + r;
-              if (t < T) o[r] += to_f32<DT>(X[(int64_t)t * K + cc]) * wv;
-            }
+            o += to_f32<DT>(X[(int64_t)t * K + cc]) * wv;
           }
-#pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            const int t = 4 * q + r;
-            if (t >= T) continue;
-            if (acc_out != nullptr) acc_out[(int64_t)t * N + col] = acc[r];
-            const float d = (float)acc[r] * (s_sca[t] * (scb_n * (1.0f / 16129.0f)));
-            out[(int64_t)t * N + col] = from_f32<DT>(d + o[r] + bias_n);
-          }
+          if (acc_out != nullptr) acc_out[(int64_t)t * N + col] = a;
+          const float d = (float)a * (s_sca[t] * (scb_n * (1.0f / 16129.0f)));
+          out[(int64_t)t * N + col] = from_f32<DT>(d + o + bias_n);
         }
       }
       __syncthreads();  // B4
