@@ -142,12 +142,10 @@ __global__ __launch_bounds__(FD_THREADS, 1) void decode_fused_kernel(
   __shared__ v4i s_red[FD_LW][64];  // each weight wave's int32 partial tile
   __shared__ uint32_t s_b1;  // activation waves past their statistics
   __shared__ uint32_t s_b2;  // activation waves done with the first block's outlier operands
-  __shared__ int8_t s_ocb[FD_OUT_LDS][16];  // CB bytes of the outlier columns, this block
+  __shared__ float s_owv[FD_OUT_LDS][16];  // recovered weights of the outlier columns, this block
   __shared__ u32x4 s_oxc[FD_OUT_LDS][16];  // the 8-column chunk of each outlier column, all 16 rows
   __shared__ int s_oxe[FD_OUT_LDS];        // the outlier column's place in its chunk
-  __shared__ float s_scb[16];              // weight row scales of the first block
   __shared__ float s_osum[16][16];         // first block's 16-bit outlier product, [token][feature]
-  __shared__ float s_owv[FD_OUT_LDS][16];  // first block: recovered outlier weights, [column][feature]
   __shared__ float s_oxv[FD_OUT_LDS][16];  // outlier columns' X values, [column][token]
 
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
@@ -299,17 +297,14 @@ __global__ __launch_bounds__(FD_THREADS, 1) void decode_fused_kernel(
 
     // the first block's 16-bit outlier product over the staged columns while
     // the weight waves run the int8 products; weight wave 0 reads it after
-    // B3.  First each recovered weight dtype(fl32(fl32(CB * SCB) / 127)) and
-    // each X value once (not once per output), then, after the activation
-    // waves meet, one (token, feature) per thread, summed in column order.
+    // B3.  First each X value once (not once per output), then, after the
+    // activation waves meet, one (token, feature) per thread over the
+    // recovered weights the weight waves staged, summed in column order.
     if (any) {
       const int n_lds = min(n_out, FD_OUT_LDS);
-      for (int i = tid; i < 32 * n_lds; i += FD_CW * 64) {
-        const int p = i >> 4, j = i & 15;  // items [0, 16 n_lds): weights; then X values
-        if (p < n_lds)
-          s_owv[p][j] = to_f32<DT>(from_f32<DT>(div127((float)s_ocb[p][j] * s_scb[j])));
-        else
-          s_oxv[p - n_lds][j] = to_f32<DT>(half_bits(s_oxc[p - n_lds][j], s_oxe[p - n_lds]));
+      for (int i = tid; i < 16 * n_lds; i += FD_CW * 64) {
+        const int p = i >> 4, j = i & 15;
+        s_oxv[p][j] = to_f32<DT>(half_bits(s_oxc[p][j], s_oxe[p]));
       }
       lds_arrive(&s_b2, lane);
       lds_wait_count(&s_b2, FD_CW);
@@ -370,11 +365,11 @@ __global__ __launch_bounds__(FD_THREADS, 1) void decode_fused_kernel(
       scb_n = SCB[cc];
       bias_n = to_f32<DT>(bsrc[cc] & bmask);
     };
-    // CB bytes of the outlier columns of this block, from registers, placed by
-    // rank; the bitmap words come from the prefix pass's registers (lane L
-    // holds words 2L and 2L + 1), so no LDS read waits in this chain.  The
-    // recovery (CB * SCB) / 127 happens where the products are summed.
-    auto stage_outlier_bytes = [&](uint32_t pp, uint32_t bw0, uint32_t bw1) {
+    // Recovered weights dtype(fl32(fl32(CB * SCB) / 127)) of the outlier
+    // columns of this block, from registers, placed by rank; the bitmap words
+    // come from the prefix pass's registers (lane L holds words 2L and
+    // 2L + 1), so no LDS read waits in this chain.
+    auto stage_outlier_weights = [&](uint32_t pp, uint32_t bw0, uint32_t bw1) {
 #pragma unroll
       for (int m = 0; m < FD_MPL; ++m) {
         const int L = lw * 16 + m;  // the lane with this m's two words (64 columns)
@@ -390,7 +385,10 @@ __global__ __launch_bounds__(FD_THREADS, 1) void decode_fused_kernel(
           const int e = __builtin_ctz(bits);
           bits &= bits - 1u;
           const int rank = (int)pre + __popc(wd & ((1u << ((k0 & 31) + e)) - 1u));
-          if (rank < FD_OUT_LDS) s_ocb[rank][nr] = (int8_t)((b[m][e >> 2] >> (8 * (e & 3))) & 0xFFu);
+          if (rank < FD_OUT_LDS) {
+            const int8_t cb = (int8_t)((b[m][e >> 2] >> (8 * (e & 3))) & 0xFFu);
+            s_owv[rank][nr] = to_f32<DT>(from_f32<DT>(div127((float)cb * scb_n)));
+          }
         }
       }
     };
@@ -407,8 +405,7 @@ __global__ __launch_bounds__(FD_THREADS, 1) void decode_fused_kernel(
     uint32_t pp = 0u, bw0 = 0u, bw1 = 0u;
     if (any) {
       pp = bitmap_prefix(s_bm, W, lane, n_out, bw0, bw1);
-      stage_outlier_bytes(pp, bw0, bw1);
-      if (lw == 0 && lane < 16) s_scb[nr] = scb_n;
+      stage_outlier_weights(pp, bw0, bw1);
     }
     const int n_lds = min(n_out, FD_OUT_LDS);
     __syncthreads();  // B2
@@ -417,7 +414,7 @@ __global__ __launch_bounds__(FD_THREADS, 1) void decode_fused_kernel(
     for (int blk = blk0; blk < nblk; blk += G) {
       if (blk != blk0) {
         load_cb(blk);
-        if (any) stage_outlier_bytes(pp, bw0, bw1);
+        if (any) stage_outlier_weights(pp, bw0, bw1);
       }
       // 16x16 layout: lane holds feature nr = lane % 16, tokens 4 q + r
       // (r = 0 .. 3).  After B3 weight wave lw finishes token 4 q + lw of
@@ -425,15 +422,12 @@ __global__ __launch_bounds__(FD_THREADS, 1) void decode_fused_kernel(
       // any order), its 16-bit outlier product, the epilogue.  The
       // activation waves sum the first block's outlier product between B2 and
       // B3; for later blocks each weight wave sums its token's itself over
-      // the CB bytes all four staged after B4 (rows beyond T hold row T - 1:
-      // they only feed outputs never stored).
+      // the recovered weights all four staged after B4 (rows beyond T hold
+      // row T - 1: they only feed outputs never stored).
       auto outlier_sum = [&](int t) {
         float o = 0.0f;
-        for (int p = 0; p < n_lds; ++p) {
-          // recovered weight dtype(fl32(fl32(CB * SCB) / 127)) of feature nr
-          const float wv = to_f32<DT>(from_f32<DT>(div127((float)s_ocb[p][nr] * scb_n)));
-          o += to_f32<DT>(reinterpret_cast<const uint16_t*>(&s_oxc[p][t])[s_oxe[p]]) * wv;
-        }
+        for (int p = 0; p < n_lds; ++p)
+          o += to_f32<DT>(reinterpret_cast<const uint16_t*>(&s_oxc[p][t])[s_oxe[p]]) * s_owv[p][nr];
         return o;
       };
       v4i acc = {0, 0, 0, 0};
