@@ -311,16 +311,29 @@ __global__ __launch_bounds__(FD_THREADS, 1) void decode_fused_kernel(
       if (tid < 256) {
         const int t = tid >> 4, n = tid & 15;
         float o = 0.0f;
-        for (int p = 0; p < n_lds; ++p) o += s_oxv[p][t] * s_owv[p][n];
+        for (int p0 = 0; p0 < n_lds; p0 += 8) {  // eight columns' operands read together, summed in order
+          float xv[8], wv[8];
+#pragma unroll
+          for (int i = 0; i < 8; ++i) {
+            const int p = min(p0 + i, n_lds - 1);
+            xv[i] = s_oxv[p][t];
+            wv[i] = s_owv[p][n];
+          }
+#pragma unroll
+          for (int i = 0; i < 8; ++i)
+            if (p0 + i < n_lds) o += xv[i] * wv[i];
+        }
         s_osum[t][n] = o;
       }
     }
 
-    // side outputs: CA shared out over the grid, the small ones by workgroup 0
+    // side outputs: CA shared out over the grid (from activation wave 4 on,
+    // the waves that sum no outlier product), the small ones by workgroup 0
     {
       const int cpr = K >> 4;  // 16-byte code chunks per row
       const int units = T * cpr;
-      for (int u = wg + G * tid; u < units; u += G * (FD_CW * 64)) {
+      const int ts = (tid + 256) & (FD_CW * 64 - 1);
+      for (int u = wg + G * ts; u < units; u += G * (FD_CW * 64)) {
         const int t = u / cpr, ch = u - t * cpr;
         *reinterpret_cast<v4i*>(CA + (int64_t)t * K + ch * 16) = *reinterpret_cast<const v4i*>(&s_codes[code_off(t, ch)]);
       }
